@@ -1,0 +1,190 @@
+"""CPU oracle for block-causal chunk attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package.  The product path (the HIP library and its binding) never does.
+
+Two independent statements of the same definition live here:
+  * ``wf_oracle.c`` (fp64, OpenMP): walks the page table chunk by chunk, two-pass softmax;
+  * ``dense.py`` (numpy fp64): gathers keys, builds an explicit block-lower-triangular mask.
+plus an e4m3 codec and block quantizer written from the OCP 8-bit float definition.
+Every function is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libwf_oracle.so")
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def build(force: bool = False) -> str:
+    """Compile libwf_oracle.so with gcc (plain C, OpenMP)."""
+    src = os.path.join(_HERE, "wf_oracle.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", src,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_attn_masked.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_double, _f64p, _f64p, _f64p, _u8p, _f64p,
+                                         _f64p, ctypes.c_int32]
+        L.oracle_attn_rows.argtypes = [ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_double, _f64p, _f64p, _f64p,
+                                       ctypes.c_int64, _i64p, _f64p, _f64p, ctypes.c_int32]
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_quantize_e4m3.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           _u8p, _f32p]
+        L.oracle_dequantize_e4m3.argtypes = [_u8p, _f32p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, _f64p]
+        L.oracle_merge_lse.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _f64p,
+                                       _f64p, _f64p, _f64p]
+        L.oracle_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _f64(x):
+    """Any array-like (numpy or torch, any float dtype) -> contiguous float64 numpy array."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def resolve_scale(table) -> float:
+    """Softmax scale: the table's value if positive, else 1/sqrt(head_dim)."""
+    s = float(table.softmax_scale)
+    return s if s > 0 else 1.0 / math.sqrt(table.head_dim)
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
+
+
+def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
+    """Attention of the query rows ``rows`` (default: all) of ``table``.
+
+    q [Lq, H, d]; pools [num_pages, page_size, H, d]; any float dtype, widened to fp64 exactly.
+    Returns (out [n, H, d], lse [n, H]) in fp64, natural log."""
+    H, d = int(table.num_heads), int(table.head_dim)
+    qd, kd, vd = _f64(q), _f64(k_pool), _f64(v_pool)
+    lq = int(sum(int(table.chunk_tokens[c]) for c in table.query_chunks))
+    assert qd.shape == (lq, H, d), (qd.shape, lq, H, d)
+    assert kd.shape == (table.num_pages, table.page_size, H, d) and vd.shape == kd.shape
+    rows = np.arange(lq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.shape[0], H, d), np.float64)
+    lse = np.empty((rows.shape[0], H), np.float64)
+    ints = [np.ascontiguousarray(a, np.int32) for a in (table.chunk_tokens, table.chunk_order,
+                                                        table.page_offsets, table.page_ids,
+                                                        table.query_chunks)]
+    rc = lib().oracle_attn_rows(len(ints[0]), _p(ints[0], _i32p), _p(ints[1], _i32p),
+                                _p(ints[2], _i32p), _p(ints[3], _i32p), int(table.num_pages),
+                                int(table.page_size), len(ints[4]), _p(ints[4], _i32p), H, d,
+                                resolve_scale(table), _p(qd, _f64p), _p(kd, _f64p), _p(vd, _f64p),
+                                rows.shape[0], _p(rows, _i64p), _p(out, _f64p), _p(lse, _f64p),
+                                int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows failed with code %d" % rc)
+    return out, lse
+
+
+def attn_masked(q, k, v, allowed, scale: float, nthreads: int = 0):
+    """One head, explicit mask: q [nq, d], k/v [nk, d], allowed [nq, nk] bool."""
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    al = np.ascontiguousarray(allowed, dtype=np.uint8)
+    nq, d = qd.shape
+    nk = kd.shape[0]
+    out = np.empty((nq, d), np.float64)
+    lse = np.empty((nq,), np.float64)
+    rc = lib().oracle_attn_masked(nq, nk, d, float(scale), _p(qd, _f64p), _p(kd, _f64p),
+                                  _p(vd, _f64p), _p(al, _u8p), _p(out, _f64p), _p(lse, _f64p),
+                                  int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_masked failed with code %d" % rc)
+    return out, lse
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    L = lib()
+    return np.array([L.oracle_e4m3_decode(int(x)) for x in c], dtype=np.float64).reshape(np.shape(codes))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    a = np.asarray(x, dtype=np.float32).ravel()
+    L = lib()
+    return np.array([L.oracle_e4m3_encode(float(v)) for v in a], dtype=np.uint8).reshape(np.shape(x))
+
+
+def quantize_e4m3(x):
+    """x [rows, H, d] (bf16 values; any float dtype) -> (x8 uint8 [rows,H,d], scales f32 [ceil(rows/64),H])."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    xf = np.ascontiguousarray(x, dtype=np.float32)
+    rows, H, d = xf.shape
+    x8 = np.empty(xf.shape, np.uint8)
+    sc = np.empty(((rows + 63) // 64, H), np.float32)
+    rc = lib().oracle_quantize_e4m3(_p(xf, _f32p), rows, H, d, _p(x8, _u8p), _p(sc, _f32p))
+    if rc != 0:
+        raise ValueError("oracle_quantize_e4m3 failed with code %d" % rc)
+    return x8, sc
+
+
+def dequantize_e4m3(x8, scales) -> np.ndarray:
+    x8 = np.ascontiguousarray(x8, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    rows, H, d = x8.shape
+    y = np.empty(x8.shape, np.float64)
+    rc = lib().oracle_dequantize_e4m3(_p(x8, _u8p), _p(sc, _f32p), rows, H, d, _p(y, _f64p))
+    if rc != 0:
+        raise ValueError("oracle_dequantize_e4m3 failed with code %d" % rc)
+    return y
+
+
+def merge_lse(o_parts, lse_parts):
+    """o_parts [p, n, d], lse_parts [p, n] -> (out [n, d], lse [n])."""
+    o = _f64(o_parts)
+    l = _f64(lse_parts)
+    p, n, d = o.shape
+    out = np.empty((n, d), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = lib().oracle_merge_lse(p, n, d, _p(o, _f64p), _p(l, _f64p), _p(out, _f64p), _p(lse, _f64p))
+    if rc != 0:
+        raise ValueError("oracle_merge_lse failed with code %d" % rc)
+    return out, lse
