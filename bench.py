@@ -1,0 +1,219 @@
+"""Benchmark of block-causal chunk attention (libwfattn.so) on one MI355X.
+
+One step = one wfattn_fwd call (every kernel of the hot path) over one DiT layer's attention of
+one chunk-stage task, with inputs resident in HBM; the plan and its upload are built once per
+round and timed separately.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--no-cpu-baseline]
+
+Default workload: the Wan-1.3B chunk task (H=12, d=128, 4680 query tokens of one chunk against
+18720 keys of the own chunk and three earlier ones, 256-token shuffled pages), bf16.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2516.6  # TFLOP/s, dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8 = 5033.2
+PEAK_MIXED = 3355.4  # e4m3 Q.K^T at the fp8 rate, P.V at the bf16 rate (equal FLOPs)
+
+
+def effective_flops(table) -> float:
+    """4 * d * H * sum over query chunks of tokens x visible keys (unmasked pairs only)."""
+    t = table
+    tot = 0
+    for a in t.query_chunks:
+        vis = sum(int(t.chunk_tokens[b]) for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a])
+        tot += int(t.chunk_tokens[a]) * vis
+    return 4.0 * t.head_dim * t.num_heads * tot
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ["attn_fwd.hip", "device.hpp", "plan.cpp", "plan.hpp"]:
+        h.update(open(os.path.join(ROOT, "block_causal_chunk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken with the
+    current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("kernel_src_sha") != kernel_src_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The oracle, as it stands, on a bounded sample of query rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    oracle.build()
+    t = case.table
+    q = case.q.double().numpy()
+    k = case.k_pool.double().numpy()
+    v = case.v_pool.double().numpy()
+    lq = t.lq
+    rng = np.random.default_rng(0)
+    n = 16
+    while True:
+        rows = np.sort(rng.choice(lq, size=min(n, lq), replace=False))
+        t0 = time.perf_counter()
+        oracle.attn_rows(t, q, k, v, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n >= lq:
+            break
+        n = min(lq, int(n * max(2.0, budget_s / max(dt, 1e-3) / 1.5)))
+    # FLOPs of the sampled rows: each row sees the visible keys of its chunk
+    qstart = np.concatenate([[0], np.cumsum([int(t.chunk_tokens[a]) for a in t.query_chunks])])
+    vis = []
+    for a in t.query_chunks:
+        vis.append(sum(int(t.chunk_tokens[b]) for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a]))
+    flops = sum(4.0 * t.head_dim * t.num_heads * vis[int(np.searchsorted(qstart, r, side="right") - 1)] for r in rows)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.max_threads(), kind="oracle",
+                sample=f"{len(rows)} of {lq} query rows (all {t.num_heads} heads), fp64, {dt:.1f} s",
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan13b_task")
+    ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--xcd-remap", type=int, default=0)
+    ap.add_argument("--cold", action="store_true", help="evict the 256 MB Infinity Cache between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (no collectives, no sharding); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_causal_chunk_amd import binding as B
+    from block_causal_chunk_amd.inputs import WORKLOADS, make_case
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    dev = torch.device("cuda:0")
+    case = make_case(args.workload)
+    t = case.table
+    fp8 = args.workload == "wan14b_fp8"
+    f32 = case.io_dtype == torch.float32
+    q, k, v = case.q.to(dev), case.k_pool.to(dev), case.v_pool.to(dev)
+    H, d = t.num_heads, t.head_dim
+
+    tp0 = time.perf_counter()
+    mode = B.WFATTN_WS_FP8 if fp8 else (B.WFATTN_WS_FP32 if f32 else B.WFATTN_WS_BF16)
+    att = B.Attention(t, device=dev, mode=mode, split_k=args.split_k, xcd_remap=args.xcd_remap)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - tp0) * 1e3
+    summary = att.plan.describe(0)
+
+    out = torch.empty((t.lq, H, d), dtype=torch.bfloat16 if not f32 else torch.float32, device=dev)
+    quant_ms = None
+    if fp8:
+        rows = k.shape[0] * k.shape[1]
+        kv = k.view(rows, H, d)
+        k8 = torch.empty((rows, H, d), dtype=torch.uint8, device=dev)
+        ks = torch.empty(((rows + 63) // 64, H), dtype=torch.float32, device=dev)
+        q8, qs = B.quantize_q_fp8(t, q)
+        B.wfattn_quantize_fp8(kv, rows, H, d, k8, ks)
+        torch.cuda.synchronize()
+        # quantization of the K pool timed on its own (it is HBM-bound and runs once per chunk)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            B.wfattn_quantize_fp8(kv, rows, H, d, k8, ks)
+        e1.record()
+        torch.cuda.synchronize()
+        quant_ms = e0.elapsed_time(e1) / 10
+        k8 = k8.view(k.shape)
+
+        def step():
+            B.wfattn_fwd_fp8(att.plan, q8, qs, k8, ks, v, out, None, att.ws)
+    else:
+        def step():
+            B.wfattn_fwd(att.plan, B.WFATTN_FP32 if f32 else B.WFATTN_BF16, q, k, v, out, None, att.ws)
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)  # untimed 512 MB write evicts the Infinity Cache
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
+    ms = float(per.mean())
+    flops = effective_flops(t)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tasks = len(t.query_chunks) / (ms * 1e-3)
+    peak = PEAK_MIXED if fp8 else PEAK_BF16
+    res = {
+        "metric": "effective attention TFLOP/s (unmasked pairs only) + chunk-tasks/s, % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 QK^T, bf16 PV" if fp8 else ("bf16 (fp32 I/O)" if f32 else "bf16"),
+        "data": "synthetic, seeded N(0,1) Q/K/V, shuffled 256-token pages",
+        "config": {"workload": args.workload, "heads": H, "head_dim": d,
+                   "query_tokens": t.lq, "key_tokens": int(sum(int(x) for x in t.chunk_tokens)),
+                   "query_chunks": len(t.query_chunks), "page_size": t.page_size,
+                   "cache": "cold" if args.cold else "warm"},
+        "tasks_per_s": round(tasks, 1),
+        "p10_ms": round(float(np.percentile(per, 10)), 4),
+        "p50_ms": round(float(np.percentile(per, 50)), 4),
+        "p90_ms": round(float(np.percentile(per, 90)), 4),
+        "effective_gflop_per_step": round(flops / 1e9, 3),
+        "plan_and_upload_ms": round(plan_ms, 3),
+        "plan": {"items": int(summary[0]), "key_tiles": int(summary[1]), "merge_groups": int(summary[2]),
+                 "splits": int(summary[6]), "block_m": int(summary[4]), "block_n": int(summary[5])},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic_from_profiles(args.workload)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if fp8:
+        res["quantize_k_pool_ms"] = round(quant_ms, 4)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        res["cpu_baseline"]["value"] = round(res["cpu_baseline"]["value"], 6)
+        res["cpu_baseline"]["seconds"] = round(res["cpu_baseline"]["seconds"], 2)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,120 @@
+// api.hip -- the extern "C" entry points that touch the device: upload, forward, quantize.
+// Every argument check runs before the first HIP call (see include/wfattn.h for the contract).
+#include <cmath>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+
+using namespace wfattn;
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+FwdParams base_params(const Plan* P, void* ws) {
+  FwdParams fp{};
+  char* w = static_cast<char*>(ws);
+  fp.blob = reinterpret_cast<const int32_t*>(w + P->ws_blob);
+  fp.part_o = reinterpret_cast<float*>(w + P->ws_part_o);
+  fp.part_lse = reinterpret_cast<float*>(w + P->ws_part_lse);
+  fp.H = P->num_heads;
+  fp.lq = static_cast<int32_t>(P->lq);
+  fp.scale = P->scale;
+  fp.c = static_cast<float>(static_cast<double>(P->scale) * 1.4426950408889634);  // scale * log2(e)
+  fp.nonce_lo = static_cast<uint32_t>(P->nonce & 0xffffffffu);
+  fp.nonce_hi = static_cast<uint32_t>(P->nonce >> 32);
+  return fp;
+}
+
+}  // namespace
+
+extern "C" wfattn_status wfattn_plan_upload(const wfattn_plan_t* plan, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return WFATTN_ERR_UNSUPPORTED;
+  const Plan* P = as_plan(plan);
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  hipError_t e = hipMemcpyAsync(static_cast<char*>(ws) + P->ws_blob, P->blob.data(), P->blob.size() * sizeof(int32_t),
+                                hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WFATTN_OK : WFATTN_ERR_DEVICE;
+}
+
+extern "C" wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q, const void* k_pool,
+                                    const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !q || !k_pool || !v_pool || !out) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  if (dtype != WFATTN_BF16 && dtype != WFATTN_FP32) return WFATTN_ERR_UNSUPPORTED;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  const Plan* P = as_plan(plan);
+  const bool f32 = dtype == WFATTN_FP32;
+  if (ws_bytes < (f32 ? P->ws_fp32_bytes : P->ws_base_bytes)) return WFATTN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FwdParams fp = base_params(P, ws);
+  fp.out = out;
+  fp.lse = lse;
+  if (f32) {
+    char* w = static_cast<char*>(ws);
+    uint16_t* sq = reinterpret_cast<uint16_t*>(w + P->stage_q_off);
+    uint16_t* sk = reinterpret_cast<uint16_t*>(w + P->stage_k_off);
+    uint16_t* sv = reinterpret_cast<uint16_t*>(w + P->stage_v_off);
+    const int64_t qn = P->lq * P->num_heads * P->head_dim;
+    const int64_t pn = P->pool_rows * P->num_heads * P->head_dim;
+    if (launch_f32_to_bf16(static_cast<const float*>(q), sq, qn, s) != hipSuccess ||
+        launch_f32_to_bf16(static_cast<const float*>(k_pool), sk, pn, s) != hipSuccess ||
+        launch_f32_to_bf16(static_cast<const float*>(v_pool), sv, pn, s) != hipSuccess)
+      return WFATTN_ERR_DEVICE;
+    fp.q = sq;
+    fp.k = sk;
+    fp.v = sv;
+  } else {
+    fp.q = static_cast<const uint16_t*>(q);
+    fp.k = static_cast<const uint16_t*>(k_pool);
+    fp.v = static_cast<const uint16_t*>(v_pool);
+  }
+  if (launch_attn_bf16(fp, P->head_dim, f32, P->n_items, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (launch_combine(fp, P->head_dim, f32, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  return WFATTN_OK;
+}
+
+extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                                        const uint8_t* k8_pool, const float* k_scale, const void* v_pool, void* out,
+                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !q8 || !q_scale || !k8_pool || !k_scale || !v_pool || !out) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(q8, 16) || !aligned(k8_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) || !aligned(q_scale, 4) ||
+      !aligned(k_scale, 4) || !aligned(lse, 4) || !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  const Plan* P = as_plan(plan);
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FwdParams fp = base_params(P, ws);
+  fp.q8 = q8;
+  fp.q_scale = q_scale;
+  fp.k8 = k8_pool;
+  fp.k_scale = k_scale;
+  fp.v = static_cast<const uint16_t*>(v_pool);
+  fp.out = out;
+  fp.lse = lse;
+  if (launch_attn_fp8(fp, P->head_dim, P->n_items, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (launch_combine(fp, P->head_dim, false, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  return WFATTN_OK;
+}
+
+extern "C" wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads, int32_t head_dim,
+                                             uint8_t* x8, float* scales, void* stream) {
+  if (!x_bf16 || !x8 || !scales) return WFATTN_ERR_NULL;
+  if (head_dim != 64 && head_dim != 128) return WFATTN_ERR_UNSUPPORTED;
+  if (rows < 0 || heads < 1) return WFATTN_ERR_RANGE;
+  if ((rows + 63) / 64 * static_cast<int64_t>(heads) > INT32_MAX) return WFATTN_ERR_RANGE;
+  if (!aligned(x_bf16, 16) || !aligned(x8, 16) || !aligned(scales, 4)) return WFATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return WFATTN_OK;
+  if (launch_quantize_fp8(static_cast<const uint16_t*>(x_bf16), rows, heads, head_dim, x8, scales,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WFATTN_ERR_DEVICE;
+  return WFATTN_OK;
+}

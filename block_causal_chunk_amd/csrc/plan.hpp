@@ -1,0 +1,65 @@
+// plan.hpp -- host-side planner state shared by plan.cpp and the launch glue (no HIP here).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/wfattn.h"
+
+namespace wfattn {
+
+// Tile geometry of the attention kernels (rows of Q per workgroup, keys per LDS tile).
+constexpr int kBlockM = 128;
+constexpr int kBlockN = 64;
+constexpr int kItemInts = 8;   // ints per work item
+constexpr int kTileInts = 2;   // ints per key tile
+constexpr int kGroupInts = 8;  // ints per combine group
+constexpr int kHeaderInts = 16;
+constexpr uint32_t kMagic = 0x57464131u;  // "WFA1"
+
+// Header words of the uploaded blob (int32 index).
+enum HeaderWord {
+  H_MAGIC = 0,
+  H_NONCE_LO = 1,
+  H_NONCE_HI = 2,
+  H_ITEMS = 3,
+  H_TILES = 4,
+  H_GROUPS = 5,
+  H_OFF_ITEMS = 6,
+  H_OFF_TILES = 7,
+  H_OFF_GROUPS = 8,
+};
+
+struct Plan {
+  uint32_t magic = kMagic;
+  uint64_t nonce = 0;
+  // table facts
+  int32_t num_chunks = 0, num_heads = 0, head_dim = 0, page_size = 0, num_pages = 0;
+  int32_t num_query_chunks = 0;
+  int64_t lq = 0;
+  int64_t nqb = 0;          // Q-scale blocks (64-row, restarting per query chunk)
+  int64_t pool_rows = 0;    // num_pages * page_size
+  float scale = 0.f;        // resolved softmax scale
+  // schedule
+  int32_t block_m = kBlockM, block_n = kBlockN, splits = 1, xcd_remap = 1;
+  int32_t n_items = 0, n_tiles = 0, n_groups = 0, n_partials = 0;
+  std::vector<int32_t> blob;  // header + items + key tiles + combine groups, uploaded verbatim
+  size_t off_items = 0, off_tiles = 0, off_groups = 0;  // int32 offsets into blob
+  // workspace layout (bytes)
+  size_t ws_blob = 0, ws_part_o = 0, ws_part_lse = 0, ws_stage = 0;
+  size_t ws_base_bytes = 0;   // blob + partials
+  size_t ws_fp32_bytes = 0;   // + bf16 staging of q and both pools
+  size_t stage_q_off = 0, stage_k_off = 0, stage_v_off = 0;
+};
+
+}  // namespace wfattn
+
+struct wfattn_plan_s {
+  wfattn::Plan impl;
+};
+
+namespace wfattn {
+inline bool plan_ok(const wfattn_plan_t* p) { return p != nullptr && p->impl.magic == kMagic; }
+inline const Plan* as_plan(const wfattn_plan_t* p) { return &p->impl; }
+}  // namespace wfattn

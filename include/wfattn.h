@@ -1,0 +1,181 @@
+/*
+ * wfattn.h -- C ABI of libwfattn.so: block-causal mixed-noise chunk attention on MI355X (gfx950).
+ *
+ * What is computed.  One call is one DiT layer's attention for every head over a query set of
+ * one or more latent chunks.  Queries attend fully to the tokens of their own chunk and to every
+ * token of every earlier, cleaner chunk, and never to a later, noisier one:
+ *   - Wave Forcing project page, "01 - The design gap", column "C - Directed live frontier":
+ *     full attention inside a chunk, block-causal across chunks;
+ *   - same page, "Key observation": only the reverse noisy -> clean edge is removed;
+ *   - KipQuest paper page, "The deep dive": the context of a chunk is the anchor, the clean
+ *     history, the live store and the earlier chunks in flight.
+ * The K/V of every chunk sit in a read-only pool of fixed-size pages that producers filled in
+ * place; attention reads its prefix where it lies, with no assembly (project page, "03 -
+ * End-to-end KV transport", "Layout" panel; KipQuest page, "The deep dive", on the paged
+ * variant).  For query row i of chunk a and head h:
+ *   o[i,h,:] = sum_j softmax_j(scale * <q[i,h,:], k_j[h,:]>) * v_j[h,:]
+ * over the keys j of every chunk b with chunk_order[b] <= chunk_order[a];
+ *   lse[h,i] = log sum_j exp(scale * <q, k_j>)   (natural log).
+ *
+ * Conventions used by every entry point.
+ *   - Device pointers are plain pointers returned by hipMalloc (or torch); the library never
+ *     allocates, frees or retains device memory, and never writes q, the pools or the scales.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *     enqueued asynchronously and nothing synchronizes; device faults surface at the caller's
+ *     next synchronization.
+ *   - Every entry point returns a status; out-parameters are written only on WFATTN_OK.  Every
+ *     check except WFATTN_ERR_DEVICE runs before the first HIP call, so nothing is enqueued when
+ *     a check fails.  Nothing prints or aborts.
+ *   - Layouts (row-major, innermost last):
+ *       q, out           [Lq, H, d]            Lq = tokens of the query chunks, concatenated
+ *       k_pool, v_pool   [num_pages, page_size, H, d]
+ *       lse              [H, Lq] fp32
+ *       q_scale          [nqb, H] fp32, nqb = sum over query chunks of ceil(tokens/64); the 64-row
+ *                        blocks restart at the first row of each query chunk
+ *       k_scale          [num_pages * page_size / 64, H] fp32 (blocks align to pages)
+ */
+#ifndef WFATTN_H
+#define WFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wfattn_status {
+  WFATTN_OK = 0,
+  WFATTN_ERR_NULL = 1,        /* a required pointer is NULL                                    */
+  WFATTN_ERR_INVALID = 2,     /* malformed table: token count < 1, order not a permutation,   */
+                              /* page count != ceil(tokens/page_size), duplicate or unknown   */
+                              /* query chunk, heads < 1, bad plan handle                      */
+  WFATTN_ERR_RANGE = 3,       /* page id out of range or used twice; a size overflows int32   */
+  WFATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128, page_size not a multiple of 64, device  */
+                              /* pointer not 16-byte aligned, dtype or option not supported   */
+  WFATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than wfattn_workspace_bytes()      */
+  WFATTN_ERR_DEVICE = 6,      /* a HIP call or kernel launch failed                           */
+  WFATTN_ERR_NOMEM = 7        /* host memory for the plan could not be allocated              */
+} wfattn_status;
+
+typedef enum wfattn_dtype {
+  WFATTN_BF16 = 0, /* q, pools and out in bf16                                                 */
+  WFATTN_FP32 = 1  /* q, pools and out in fp32; converted to bf16 in the workspace, computed   */
+                   /* in bf16 like WFATTN_BF16, output written in fp32                         */
+} wfattn_dtype;
+
+/* Workspace modes for wfattn_workspace_bytes. */
+#define WFATTN_WS_BF16 0
+#define WFATTN_WS_FP32 1
+#define WFATTN_WS_FP8 2
+
+/* One round's chunk table.  All arrays are host memory; wfattn_plan copies what it needs. */
+typedef struct wfattn_chunk_table {
+  int32_t num_chunks;           /* chunks whose K/V are in the pool, query chunks included      */
+  const int32_t* chunk_tokens;  /* [num_chunks], each >= 1                                      */
+  const int32_t* chunk_order;   /* [num_chunks], a permutation of 0..num_chunks-1; 0 = cleanest */
+                                /* (oldest).  Key chunk b is visible to query chunk a iff       */
+                                /* chunk_order[b] <= chunk_order[a].  A strict order: a tie     */
+                                /* would be a two-way edge, which the method removes.           */
+  const int32_t* page_offsets;  /* [num_chunks+1], CSR into page_ids; chunk c owns exactly      */
+                                /* ceil(chunk_tokens[c]/page_size) pages, token u of chunk c is */
+                                /* in page page_ids[page_offsets[c] + u/page_size], slot        */
+                                /* u % page_size                                                */
+  const int32_t* page_ids;      /* [page_offsets[num_chunks]], physical page ids, each in       */
+                                /* [0, num_pages) and used at most once                         */
+  int32_t num_pages;            /* pool capacity in pages                                       */
+  int32_t page_size;            /* tokens per page, a positive multiple of 64                   */
+  int32_t num_query_chunks;     /* >= 1                                                         */
+  const int32_t* query_chunks;  /* [num_query_chunks], distinct chunk ids; Q/out rows are their */
+                                /* tokens concatenated in this order                            */
+  int32_t num_heads;            /* H, the same for Q and K/V                                    */
+  int32_t head_dim;             /* d: 64 or 128                                                 */
+  float softmax_scale;          /* <= 0 means 1/sqrt(head_dim)                                  */
+} wfattn_chunk_table;
+
+/* Planner options; zero-initialise for defaults. */
+typedef struct wfattn_opts {
+  int32_t split_k;   /* 0: the planner decides; 1: never split a query tile's keys; n > 1: split */
+                     /* every query tile's key range into up to n parts merged through the LSE   */
+  int32_t xcd_remap; /* 0: default (on); 1: on; -1: off.  Groups one head's work on one XCD     */
+  int32_t reserved0; /* must be 0 */
+  int32_t reserved1; /* must be 0 */
+} wfattn_opts;
+
+typedef struct wfattn_plan_s wfattn_plan_t; /* opaque, host memory only, immutable once built   */
+
+/* Validate `table` and build the work list: for each query chunk its visible key prefix in
+ * clean -> noisy order, query tiles that never cross a chunk, key tiles that never cross a page,
+ * and a schedule over the CUs.  Host only, no HIP call.  The plan owns copies of everything it
+ * needs; free it with wfattn_plan_free.  Errors: NULL, INVALID, RANGE, UNSUPPORTED, NOMEM. */
+wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfattn_opts* opts /* NULL ok */,
+                          wfattn_plan_t** plan_out);
+void wfattn_plan_free(wfattn_plan_t* plan); /* NULL ok */
+
+/* Lq of the plan (rows of q/out), or -1 for a NULL plan. */
+int64_t wfattn_query_rows(const wfattn_plan_t* plan);
+
+/* Bytes of device workspace wfattn_fwd (mode WFATTN_WS_BF16 / _FP32) or wfattn_fwd_fp8
+ * (WFATTN_WS_FP8) needs with this plan; 0 for a NULL plan or unknown mode.  The workspace holds
+ * the uploaded work list and page table, split-K partials and (fp32 mode) bf16 staging. */
+size_t wfattn_workspace_bytes(const wfattn_plan_t* plan, int32_t mode);
+
+/* Copy the plan's work list and page table into `ws` on `stream` (asynchronous; the plan must
+ * stay alive until the copy has run).  Do it once per round; every wfattn_fwd / wfattn_fwd_fp8
+ * with this plan then reuses the workspace.  Errors: NULL, INVALID, WORKSPACE, UNSUPPORTED
+ * (ws not 256-byte aligned), DEVICE. */
+wfattn_status wfattn_plan_upload(const wfattn_plan_t* plan, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Introspection for host tests.  what = 0: summary, 8 int32 (items, key tiles, combine groups,
+ * partial slots, block_m, block_n, splits used, query chunks); what = 1: work items, 8 int32
+ * each (head, first Q row, rows, first key tile, end key tile, partial slot or -1, first Q-scale
+ * block, query chunk index) in launch order; what = 2: key tiles, 2 int32 each (first pool row,
+ * valid keys); what = 3: combine groups, 8 int32 each (head, first Q row, rows, first partial
+ * slot, parts, 0, 0, 0).  Copies min(cap, total) int32 into buf (buf may be NULL when cap == 0)
+ * and stores the total count of int32 in *n. */
+wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t what, int32_t* buf,
+                                   size_t cap, size_t* n);
+
+/* bf16 (or fp32 I/O) forward.  q, k_pool, v_pool, out in `dtype`; lse NULL or [H, Lq] fp32.
+ * ws must hold wfattn_workspace_bytes(plan, dtype == WFATTN_FP32 ? WFATTN_WS_FP32 :
+ * WFATTN_WS_BF16) bytes and have been filled by wfattn_plan_upload from this plan.  Device
+ * pointers must be 16-byte aligned (ws 256-byte).  Padding slots of the pools are never read.
+ * Concurrent calls on different streams need different workspaces.
+ * Errors: NULL, INVALID, UNSUPPORTED, WORKSPACE, DEVICE. */
+wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
+                         const void* k_pool, const void* v_pool, void* out, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Forward with e4m3 (OCP E4M3FN) Q.K^T: q8 [Lq,H,d] and k8_pool [num_pages,page_size,H,d] are
+ * e4m3 codes with one fp32 scale per (64-row block, head) (value = decode(code) * scale, the
+ * layout of q_scale / k_scale is given at the top of this file); v_pool and out are bf16.
+ * Scores are accumulated in fp32 and scaled once per block pair; P.V runs in bf16.
+ * ws: wfattn_workspace_bytes(plan, WFATTN_WS_FP8).  Errors as wfattn_fwd. */
+wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                             const uint8_t* k8_pool, const float* k_scale, const void* v_pool,
+                             void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Block quantizer: x_bf16 [rows, heads, head_dim] -> x8 (e4m3 codes, same shape) and
+ * scales [ceil(rows/64), heads].  For each block of 64 consecutive rows (the last may be short)
+ * and head: amax = max |x| over the block (NaN ignored), scale = amax/448, code = round-to-
+ * nearest-even e4m3 of x * (448/amax) clamped to [-448, 448]; amax == 0 gives scale 1.  All in
+ * fp32.  The K pool is quantized as rows = num_pages*page_size; Q once per query chunk (pass the
+ * chunk's first row and its first scale block).  The reduced-precision K/V transport is the
+ * project page's "03 - End-to-end KV transport", "Precision" panel.
+ * Errors: NULL, UNSUPPORTED (head_dim not 64/128, pointers not 16-byte aligned), RANGE
+ * (rows < 0 or heads < 1), DEVICE. */
+wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads,
+                                  int32_t head_dim, uint8_t* x8, float* scales, void* stream);
+
+/* Static string naming a status. */
+const char* wfattn_status_str(wfattn_status status);
+
+/* ABI version of this header: 1. */
+int32_t wfattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WFATTN_H */

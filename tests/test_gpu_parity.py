@@ -1,0 +1,308 @@
+"""GPU parity: libwfattn.so (through its C ABI) against the fp64 CPU oracle on the same seeded
+inputs.  Small and medium cases are compared on every output element; the five full-size
+workloads, in the launch configuration bench.py times, on sampled rows the oracle computes one by
+one.  Invariants of the method are checked bitwise."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from block_causal_chunk_amd.inputs import fill_case, make_case, make_table
+from helpers import check_bf16, check_contract_bf16, check_fp8_contract, f64, sample_rows, stats, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["tiny_fp32", "wan13b_task", "wave_round", "long_rollout", "wan14b_fp8"]
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_causal_chunk_amd import binding
+    binding.lib()  # raises if the library is missing: no fallback
+    return binding
+
+
+@pytest.fixture(scope="module")
+def O():
+    import oracle
+    oracle.build()
+    return oracle
+
+
+def run(B, case, split_k=0, xcd=0, want_lse=True):
+    q, k, v = to_dev(case)
+    mode = B.WFATTN_WS_FP32 if case.io_dtype == torch.float32 else B.WFATTN_WS_BF16
+    att = B.Attention(case.table, mode=mode, split_k=split_k, xcd_remap=xcd)
+    out, lse = att.fwd(q, k, v, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return out, lse, att
+
+
+def medium_case(name, seed=77):
+    """Chunks of 300 tokens (three query tiles, the last ragged), 256-token pages (the second page
+    of a chunk holds 44 keys), 3 heads; the chunk structure of the named workload."""
+    from block_causal_chunk_amd.inputs import WORKLOADS
+    w = WORKLOADS[name]
+    rng = np.random.default_rng(seed)
+    t = make_table([300] * len(w["tokens"]), list(range(len(w["tokens"]))), w["queries"], 256, 3, w["d"],
+                   shuffle_rng=rng, spare=3)
+    return fill_case(name + "_medium", t, rng, torch.bfloat16, w.get("outlier_frac", 0.0), w.get("outlier_mult", 1.0))
+
+
+# ------------------------------------------------------------------ bf16 / fp32-I/O forward
+@pytest.mark.parametrize("split_k", [1, 0, 3])
+@pytest.mark.parametrize("name", NAMES[:4])
+def test_small_all_elements(B, O, name, split_k):
+    c = make_case(name, small=True)
+    print(f"[case] small {name} split_k={split_k}", flush=True)
+    out, lse, _ = run(B, c, split_k=split_k)
+    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    if c.io_dtype == torch.float32:
+        # fp32 is an I/O format: the contract gates hold against the fp32 inputs, the self gates
+        # against the oracle on the bf16-rounded inputs the kernel computes with
+        check_contract_bf16(f64(out), ref, name)
+        bq, bk, bv = (x.to(torch.bfloat16) for x in (c.q, c.k_pool, c.v_pool))
+        ref, ref_lse = O.attn_rows(c.table, bq, bk, bv)
+    check_bf16(f64(out), ref, name)
+    assert np.abs(f64(lse).T - ref_lse).max() <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])
+@pytest.mark.parametrize("xcd", [0, -1])
+def test_medium_all_elements(B, O, name, xcd):
+    c = medium_case(name)
+    print(f"[case] medium {name} xcd={xcd}", flush=True)
+    out, lse, att = run(B, c, xcd=xcd)
+    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    check_bf16(f64(out), ref, name)
+    assert np.abs(f64(lse).T - ref_lse).max() <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])
+def test_full_size_sampled_rows(B, O, name):
+    c = make_case(name)
+    print(f"[case] full {name}", flush=True)
+    out, lse, _ = run(B, c)  # default plan: the configuration bench.py times
+    rows = sample_rows(c.table.lq, n=32)
+    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, rows=rows)
+    got = f64(out)[rows]
+    assert np.isfinite(f64(out)).all()
+    check_bf16(got, ref, name)
+    assert np.abs(f64(lse).T[rows] - ref_lse).max() <= 2e-3
+
+
+def test_degenerate_tables(B, O):
+    """One-token chunks, a query chunk that sees only itself, head_dim 64 with bf16, a single
+    head, chunk sizes at exact tile multiples, 512-token pages, queries listed out of order."""
+    rng = np.random.default_rng(31)
+    cases = [
+        ([1], [0], [0], 64, 1, 128),
+        ([1, 1, 1], [2, 0, 1], [0, 1, 2], 64, 2, 64),
+        ([128, 256, 64], [0, 1, 2], [2, 0], 128, 2, 128),
+        ([700, 33, 513], [1, 2, 0], [1, 0, 2], 512, 3, 128),
+        ([5, 64, 65, 129], [3, 1, 0, 2], [0, 3], 64, 1, 64),
+    ]
+    for tok, order, q, page, H, d in cases:
+        print(f"[case] degenerate {tok} {order} {q} page={page} H={H} d={d}", flush=True)
+        t = make_table(tok, order, q, page, H, d, shuffle_rng=rng, spare=2)
+        c = fill_case("deg", t, rng, torch.bfloat16)
+        for split in (1, 0, 4):
+            out, lse, _ = run(B, c, split_k=split)
+            ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+            check_bf16(f64(out), ref, str(tok))
+            assert np.abs(f64(lse).T - ref_lse).max() <= 2e-3
+
+
+# ------------------------------------------------------------------ invariants (bitwise)
+def test_page_shuffle_is_bitwise_identical(B):
+    c = medium_case("long_rollout", seed=5)
+    out1, lse1, _ = run(B, c)
+    t = c.table
+    rng = np.random.default_rng(123)
+    newn = t.num_pages + 4
+    perm = rng.permutation(newn).astype(np.int32)
+    k2 = torch.full((newn,) + tuple(c.k_pool.shape[1:]), float("nan"), dtype=c.k_pool.dtype)
+    v2 = k2.clone()
+    t2 = t.copy()
+    t2.num_pages = newn
+    for lp in range(int(t.page_offsets[-1])):
+        k2[perm[lp]] = c.k_pool[int(t.page_ids[lp])]
+        v2[perm[lp]] = c.v_pool[int(t.page_ids[lp])]
+        t2.page_ids[lp] = perm[lp]
+    c2 = type(c)(c.name, t2, c.io_dtype, c.q, k2, v2)
+    out2, lse2, _ = run(B, c2)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_appending_later_chunks_is_bitwise_identical(B):
+    rng = np.random.default_rng(17)
+    base = make_table([300, 300, 300], [0, 1, 2], [1, 2], 256, 3, 128, shuffle_rng=rng, spare=1)
+    c = fill_case("base", base, rng, torch.bfloat16)
+    out1, lse1, _ = run(B, c)
+    # two later chunks (orders 3, 4) with huge K/V appended behind the existing pages
+    t2 = make_table([300, 300, 300, 200, 100], [0, 1, 2, 3, 4], [1, 2], 256, 3, 128)
+    extra = int(t2.page_offsets[-1]) - int(base.page_offsets[-1])
+    t2.num_pages = base.num_pages + extra
+    t2.page_ids = np.concatenate([base.page_ids, base.num_pages + np.arange(extra)]).astype(np.int32)
+    shape = (t2.num_pages,) + tuple(c.k_pool.shape[1:])
+    k2 = torch.full(shape, 30.0, dtype=torch.bfloat16)
+    v2 = torch.full(shape, -30.0, dtype=torch.bfloat16)
+    k2[: base.num_pages] = c.k_pool
+    v2[: base.num_pages] = c.v_pool
+    c2 = type(c)("app", t2, c.io_dtype, c.q, k2, v2)
+    out2, lse2, _ = run(B, c2)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_multi_chunk_call_equals_single_chunk_calls(B):
+    """A wave round (5 query chunks in one call) equals one call per chunk over its own prefix;
+    bitwise when every query tile keeps its whole key range (split_k = 1)."""
+    c = medium_case("wave_round", seed=9)
+    out, lse, _ = run(B, c, split_k=1)
+    row = 0
+    for i, a in enumerate(c.table.query_chunks):
+        n = int(c.table.chunk_tokens[a])
+        t1 = c.table.copy()
+        t1.query_chunks = np.array([a], np.int32)
+        c1 = type(c)("one", t1, c.io_dtype, c.q[row:row + n].contiguous(), c.k_pool, c.v_pool)
+        o1, l1, _ = run(B, c1, split_k=1)
+        assert torch.equal(o1, out[row:row + n]) and torch.equal(l1, lse[:, row:row + n])
+        row += n
+
+
+def test_deterministic_and_inputs_untouched(B):
+    c = make_case("wan13b_task")
+    q, k, v = to_dev(c)
+
+    def h(t):
+        return hashlib.sha256(t.view(torch.uint8).cpu().numpy().tobytes()).hexdigest()
+
+    hk, hv, hq = h(k), h(v), h(q)
+    att = B.Attention(c.table)
+    o1, l1 = att.fwd(q, k, v, want_lse=True)
+    o2, l2 = att.fwd(q, k, v, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert (h(k), h(v), h(q)) == (hk, hv, hq)
+    assert torch.isfinite(o1).all()  # NaN padding and spare pages never read
+
+
+def test_stale_workspace_is_ignored(B):
+    """A workspace uploaded for another plan does not match the plan's nonce: the kernels do
+    nothing instead of reading a foreign work list."""
+    c = make_case("wan13b_task", small=True)
+    q, k, v = to_dev(c)
+    a1 = B.Attention(c.table)
+    a2 = B.Attention(c.table)
+    out = torch.full((a1.lq, c.table.num_heads, c.table.head_dim), 7.0, dtype=torch.bfloat16, device="cuda")
+    B.wfattn_fwd(a1.plan, B.WFATTN_BF16, q, k, v, out, None, a2.ws)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+# ------------------------------------------------------------------ fp8
+def _quant_compare(O, x_cpu, codes_gpu, scales_gpu):
+    ref8, ref_sc = O.quantize_e4m3(x_cpu)
+    g8 = codes_gpu.cpu().numpy()
+    gs = scales_gpu.cpu().numpy()
+    xf = x_cpu.float().numpy()
+    nan = np.isnan(xf)
+    assert np.array_equal(g8[~nan], ref8[~nan])  # bit-exact on every real value
+    assert np.isin(g8[nan], [0x7F, 0xFF]).all()  # NaN padding stays NaN
+    assert np.array_equal(gs, ref_sc)
+
+
+def test_quantizer_bit_exact(B, O):
+    for name in ["wan14b_fp8", "wave_round"]:
+        for small in (True, False):
+            c = make_case(name, small=small)
+            print(f"[case] quantize {name} small={small}", flush=True)
+            q = c.q.cuda()
+            kp = c.k_pool.cuda()
+            rows = c.k_pool.shape[0] * c.k_pool.shape[1]
+            k8, ks = B.quantize_fp8(kp.view(rows, c.table.num_heads, c.table.head_dim))
+            q8, qs = B.quantize_q_fp8(c.table, q)
+            torch.cuda.synchronize()
+            _quant_compare(O, c.k_pool.reshape(rows, c.table.num_heads, c.table.head_dim), k8, ks)
+            # Q: blocks restart at each query chunk
+            row = 0
+            blk = 0
+            for a in c.table.query_chunks:
+                n = int(c.table.chunk_tokens[a])
+                nb = (n + 63) // 64
+                _quant_compare(O, c.q[row:row + n], q8[row:row + n], qs[blk:blk + nb])
+                row += n
+                blk += nb
+    # odd shapes: a short last block, head_dim 64, an all-zero block
+    x = torch.randn(130, 3, 64).to(torch.bfloat16)
+    x[64:128, 1] = 0
+    x8, sc = B.quantize_fp8(x.cuda())
+    torch.cuda.synchronize()
+    _quant_compare(O, x, x8, sc)
+
+
+def run_fp8(B, c, split_k=0):
+    H, d = c.table.num_heads, c.table.head_dim
+    q = c.q.cuda()
+    kp = c.k_pool.cuda()
+    vp = c.v_pool.cuda()
+    rows = kp.shape[0] * kp.shape[1]
+    k8, ks = B.quantize_fp8(kp.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(c.table, q)
+    att = B.Attention(c.table, mode=B.WFATTN_WS_FP8, split_k=split_k)
+    out, lse = att.fwd_fp8(q8, qs, k8.view(kp.shape), ks, vp, want_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _dequantized_case(O, c):
+    """The oracle's own quantization of Q (per query chunk) and K, dequantized in fp64."""
+    H, d = c.table.num_heads, c.table.head_dim
+    rows = c.k_pool.shape[0] * c.k_pool.shape[1]
+    k8, ks = O.quantize_e4m3(c.k_pool.reshape(rows, H, d))
+    kdq = O.dequantize_e4m3(k8, ks).reshape(c.k_pool.shape)
+    qdq = []
+    row = 0
+    for a in c.table.query_chunks:
+        n = int(c.table.chunk_tokens[a])
+        x8, sc = O.quantize_e4m3(c.q[row:row + n])
+        qdq.append(O.dequantize_e4m3(x8, sc))
+        row += n
+    return np.concatenate(qdq), kdq
+
+
+@pytest.mark.parametrize("name", ["wan14b_fp8", "wave_round"])
+@pytest.mark.parametrize("split_k", [1, 0])
+def test_fp8_small_all_elements(B, O, name, split_k):
+    c = make_case(name, small=True)
+    print(f"[case] fp8 small {name} split_k={split_k}", flush=True)
+    out, lse = run_fp8(B, c, split_k)
+    got = f64(out)
+    qdq, kdq = _dequantized_case(O, c)
+    ref_dq, ref_dq_lse = O.attn_rows(c.table, qdq, kdq, c.v_pool)  # diagnostic: the kernel's own arithmetic
+    check_bf16(got, ref_dq, name + " (dequantized oracle)")
+    assert np.abs(f64(lse).T - ref_dq_lse).max() <= 2e-3
+    ref, _ = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)  # contract: unquantized inputs
+    s = stats(got, ref)
+    print(f"fp8 vs unquantized oracle: {s}", flush=True)
+    if name == "wan14b_fp8":
+        # the fp8 contract is stated for N(0,1) inputs; with x8 outlier K channels one scale per
+        # 64x128 block costs the other channels their precision, so only the diagnostic applies
+        check_fp8_contract(got, ref, name)
+
+
+def test_fp8_full_size_sampled_rows(B, O):
+    c = make_case("wan14b_fp8")
+    print("[case] fp8 full wan14b_fp8", flush=True)
+    out, _ = run_fp8(B, c)
+    got = f64(out)
+    assert np.isfinite(got).all()
+    rows = sample_rows(c.table.lq, n=24)
+    ref, _ = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, rows=rows)
+    s = check_fp8_contract(got[rows], ref, "wan14b_fp8")
+    print("fp8 contract stats", s)
+    qdq, kdq = _dequantized_case(O, c)
+    ref_dq, _ = O.attn_rows(c.table, qdq, kdq, c.v_pool, rows=rows)
+    check_bf16(got[rows], ref_dq, "wan14b_fp8 (dequantized oracle)")

@@ -1,0 +1,235 @@
+"""Host-side tests of libwfattn.so: exported symbols, every error a host can force, and the
+schedule's coverage of the block-causal mask.  No compute call is made (no GPU here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_causal_chunk_amd.inputs import make_case, make_table
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from block_causal_chunk_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from block_causal_chunk_amd import build
+        build.build()
+    return binding
+
+
+def test_exports_every_declared_symbol(B):
+    hdr = open(os.path.join(ROOT, "include", "wfattn.h")).read()
+    declared = set(re.findall(r"\b(wfattn_[a-z0-9_]+)\s*\(", hdr))
+    assert declared == set(B.EXPORTED)
+    L = B.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.wfattn_abi_version() == 1
+    for s in range(8):
+        assert B.status_str(s) and B.status_str(s) != "unknown status"
+
+
+def _plan_status(B, t, **opts):
+    c, keep = B.make_table_c(t)
+    o = B.OptsC(opts.get("split_k", 0), opts.get("xcd_remap", 0), opts.get("r0", 0), 0)
+    h = ctypes.c_void_p()
+    st = B.lib().wfattn_plan(ctypes.byref(c), ctypes.byref(o), ctypes.byref(h))
+    if st == 0:
+        B.lib().wfattn_plan_free(h)
+    return st
+
+
+def _base():
+    return make_table([100, 70, 130], [0, 1, 2], [1, 2], 64, 2, 128, shuffle_rng=np.random.default_rng(1), spare=2)
+
+
+def test_plan_errors(B):
+    assert _plan_status(B, _base()) == B.WFATTN_OK
+    L = B.lib()
+    h = ctypes.c_void_p()
+    assert L.wfattn_plan(None, None, ctypes.byref(h)) == B.WFATTN_ERR_NULL
+    c, keep = B.make_table_c(_base())
+    assert L.wfattn_plan(ctypes.byref(c), None, None) == B.WFATTN_ERR_NULL
+    c.page_ids = None
+    assert L.wfattn_plan(ctypes.byref(c), None, ctypes.byref(h)) == B.WFATTN_ERR_NULL
+
+    def mod(**kw):
+        t = _base()
+        for k, v in kw.items():
+            setattr(t, k, v)
+        return _plan_status(B, t)
+
+    assert mod(chunk_tokens=np.array([100, 0, 130], np.int32)) == B.WFATTN_ERR_INVALID
+    assert mod(chunk_order=np.array([0, 1, 1], np.int32)) == B.WFATTN_ERR_INVALID  # a tie
+    assert mod(chunk_order=np.array([0, 1, 3], np.int32)) == B.WFATTN_ERR_INVALID
+    t = _base()
+    t.page_offsets = np.array([0, 2, 3, 6], np.int32)  # chunk 1 needs 2 pages, gets 1
+    assert _plan_status(B, t) == B.WFATTN_ERR_INVALID
+    assert mod(query_chunks=np.array([1, 1], np.int32)) == B.WFATTN_ERR_INVALID
+    assert mod(query_chunks=np.array([3], np.int32)) == B.WFATTN_ERR_INVALID
+    assert mod(num_heads=0) == B.WFATTN_ERR_INVALID
+    assert mod(softmax_scale=float("nan")) == B.WFATTN_ERR_INVALID
+    t = _base()
+    t.page_ids = t.page_ids.copy()
+    t.page_ids[3] = t.num_pages  # out of range
+    assert _plan_status(B, t) == B.WFATTN_ERR_RANGE
+    t.page_ids[3] = t.page_ids[0]  # reused
+    assert _plan_status(B, t) == B.WFATTN_ERR_RANGE
+    assert mod(head_dim=96) == B.WFATTN_ERR_UNSUPPORTED
+    t = make_table([100, 70], [0, 1], [1], 32, 2, 128)  # page_size not a multiple of 64
+    assert _plan_status(B, t) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), r0=1) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), split_k=-1) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), xcd_remap=2) == B.WFATTN_ERR_UNSUPPORTED
+    t = make_table([100], [0], [0], 64, 2, 128)
+    t.num_pages = 2 ** 26  # pool rows overflow int32
+    assert _plan_status(B, t) == B.WFATTN_ERR_RANGE
+
+
+def test_call_errors_before_any_hip_call(B):
+    """Every check except DEVICE fires before the first HIP call, so fake addresses are safe."""
+    plan = B.wfattn_plan(_base())
+    L = B.lib()
+    ws_need = plan.workspace_bytes(B.WFATTN_WS_BF16)
+    assert ws_need > 0 and plan.workspace_bytes(B.WFATTN_WS_FP32) > ws_need
+    assert plan.workspace_bytes(9) == 0
+    A = 1 << 20  # a fake, aligned address that is never dereferenced
+    h = plan.handle
+    assert L.wfattn_fwd(h, 0, None, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd(None, 0, A, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd(h, 5, A, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd(h, 0, A + 8, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd(h, 0, A, A, A, A, A + 2, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd(h, 0, A, A, A, A, None, A + 16, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd(h, 0, A, A, A, A, None, None, ws_need, None) == B.WFATTN_ERR_WORKSPACE
+    assert L.wfattn_fwd(h, 0, A, A, A, A, None, A, ws_need - 1, None) == B.WFATTN_ERR_WORKSPACE
+    assert L.wfattn_fwd(h, 1, A, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_WORKSPACE  # fp32 needs staging
+    bogus = ctypes.create_string_buffer(64)  # not a plan
+    assert L.wfattn_fwd(ctypes.addressof(bogus), 0, A, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_INVALID
+    assert L.wfattn_fwd_fp8(h, A, A, A, None, A, A, None, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd_fp8(h, A, A + 2, A, A, A, A, None, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd_fp8(h, A, A, A, A, A, A, None, A, 16, None) == B.WFATTN_ERR_WORKSPACE
+    assert L.wfattn_plan_upload(h, None, ws_need, None) == B.WFATTN_ERR_WORKSPACE
+    assert L.wfattn_plan_upload(h, A + 64, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_plan_upload(h, A, 8, None) == B.WFATTN_ERR_WORKSPACE
+    assert L.wfattn_plan_upload(None, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_quantize_fp8(None, 10, 2, 128, A, A, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_quantize_fp8(A, 10, 2, 96, A, A, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_quantize_fp8(A, -1, 2, 128, A, A, None) == B.WFATTN_ERR_RANGE
+    assert L.wfattn_quantize_fp8(A, 10, 0, 128, A, A, None) == B.WFATTN_ERR_RANGE
+    assert L.wfattn_quantize_fp8(A + 8, 10, 2, 128, A, A, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_quantize_fp8(A, 0, 2, 128, A, A, None) == B.WFATTN_OK  # nothing to do, no launch
+    assert L.wfattn_query_rows(None) == -1
+    assert L.wfattn_workspace_bytes(None, 0) == 0
+    n = ctypes.c_size_t()
+    assert L.wfattn_plan_describe(h, 7, None, 0, ctypes.byref(n)) == B.WFATTN_ERR_INVALID
+
+
+def _owner_of_pool_row(t):
+    """physical pool row -> (chunk, token) for every valid slot."""
+    own = {}
+    for b in range(t.num_chunks):
+        for lp in range(int(t.page_offsets[b]), int(t.page_offsets[b + 1])):
+            u0 = (lp - int(t.page_offsets[b])) * t.page_size
+            for u in range(u0, min(u0 + t.page_size, int(t.chunk_tokens[b]))):
+                own[int(t.page_ids[lp]) * t.page_size + u - u0] = (b, u)
+    return own
+
+
+def _check_schedule(B, t, **kw):
+    plan = B.wfattn_plan(t, **kw)
+    summ = plan.describe(0)
+    n_items, n_tiles, n_groups, n_parts, bm, bn = [int(x) for x in summ[:6]]
+    items = plan.describe(1).reshape(-1, 8)
+    tiles = plan.describe(2).reshape(-1, 2)
+    groups = plan.describe(3).reshape(-1, 8)
+    assert items.shape[0] == n_items and tiles.shape[0] == n_tiles and groups.shape[0] == n_groups
+    own = _owner_of_pool_row(t)
+    # query row -> query chunk
+    qstart = np.concatenate([[0], np.cumsum([int(t.chunk_tokens[a]) for a in t.query_chunks])])
+    seen = {}
+    slots = set()
+    for head, r0, rows, k0, k1, slot, qsb, qi in items:
+        if head < 0:
+            assert k0 == k1 == 0
+            continue
+        assert 0 <= head < t.num_heads and 1 <= rows <= bm and 0 <= k0 < k1 <= n_tiles
+        assert qstart[qi] <= r0 and r0 + rows <= qstart[qi + 1]  # a query tile never crosses a chunk
+        assert (r0 - qstart[qi]) % bm == 0
+        a = int(t.query_chunks[qi])
+        if slot >= 0:
+            assert slot not in slots
+            slots.add(slot)
+        for kt in range(k0, k1):
+            row0, nv = tiles[kt]
+            assert 1 <= nv <= bn
+            b0, u0 = own[int(row0)]
+            for j in range(nv):
+                b, u = own[int(row0) + j]
+                assert b == b0 and u == u0 + j  # a key tile never crosses a page or a chunk
+                assert t.chunk_order[b] <= t.chunk_order[a]  # no masked pair is ever enumerated
+                key = (int(head), int(r0), b, u)
+                assert key not in seen  # exactly once
+                seen[key] = True
+    # every visible (head, query tile, key) appears
+    expect = 0
+    for qi, a in enumerate(t.query_chunks):
+        vis = sum(int(t.chunk_tokens[b]) for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a])
+        n_qt = -(-int(t.chunk_tokens[a]) // bm)
+        expect += vis * n_qt * t.num_heads
+    assert len(seen) == expect
+    assert len(slots) == n_parts
+    # merge groups cover exactly the split items
+    gsl = set()
+    for head, r0, rows, s0, parts, *_ in groups:
+        assert parts >= 2
+        gsl.update(range(s0, s0 + parts))
+    assert gsl == slots
+    return plan, items, tiles
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "wan13b_task", "wave_round", "long_rollout", "wan14b_fp8"])
+def test_schedule_covers_mask_small(B, name):
+    c = make_case(name, small=True)
+    for split in (0, 1, 3):
+        for x in (0, -1):
+            _check_schedule(B, c.table, split_k=split, xcd_remap=x)
+
+
+def test_schedule_random_tables(B):
+    rng = np.random.default_rng(5)
+    for _ in range(10):
+        n = int(rng.integers(1, 7))
+        tok = rng.integers(1, 400, size=n)
+        t = make_table(tok, rng.permutation(n), rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False),
+                       int(rng.choice([64, 128, 256])), int(rng.integers(1, 4)), int(rng.choice([64, 128])),
+                       shuffle_rng=rng, spare=int(rng.integers(0, 4)))
+        _check_schedule(B, t, split_k=int(rng.integers(0, 5)))
+
+
+def test_schedule_full_size_tables_and_xcd_grouping(B):
+    """The five workloads' tables (sizes only; no values are drawn)."""
+    from block_causal_chunk_amd.inputs import WORKLOADS
+    for name, w in WORKLOADS.items():
+        t = make_table(w["tokens"], list(range(len(w["tokens"]))), w["queries"], w["page"], w["H"], w["d"],
+                       shuffle_rng=np.random.default_rng(0), spare=w["spare"])
+        plan = B.wfattn_plan(t)
+        items = plan.describe(1).reshape(-1, 8)
+        cost = np.zeros(8)
+        heads = [set() for _ in range(8)]
+        for i, it in enumerate(items):
+            if it[0] >= 0:
+                cost[i % 8] += it[4] - it[3] + 1
+                heads[i % 8].add(int(it[0]))
+        assert cost.max() <= 1.15 * cost.mean() + 64, (name, cost)
+        if name != "tiny_fp32":
+            # each XCD streams the K/V of few heads
+            assert max(len(h) for h in heads) <= -(-w["H"] // 8) + 2, (name, heads)
+    # sizes of the workload tables
+    t = make_table([4680] * 4, [0, 1, 2, 3], [3], 256, 12, 128)
+    tiles = B.wfattn_plan(t, split_k=1).describe(2).reshape(-1, 2)
+    assert tiles.shape[0] == 4 * (18 * 4 + 2) and tiles[:, 1].sum() == 4 * 4680
