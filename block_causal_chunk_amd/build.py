@@ -27,6 +27,9 @@ def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             # never emit packed fp32 math (v_pk_fma_f32 & co.)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPRs: with AGPR-form accumulators the allocator moves the
+            # O tile between AGPRs and VGPRs around every MFMA group of the attention loop
+            "-mllvm", "-amdgpu-mfma-vgpr-form=true",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

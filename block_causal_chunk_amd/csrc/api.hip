@@ -75,7 +75,7 @@ extern "C" wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtyp
     fp.k = static_cast<const uint16_t*>(k_pool);
     fp.v = static_cast<const uint16_t*>(v_pool);
   }
-  if (launch_attn_bf16(fp, P->head_dim, f32, P->n_items, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (launch_attn_bf16(fp, P->head_dim, f32, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (launch_combine(fp, P->head_dim, f32, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   return WFATTN_OK;
 }
@@ -100,7 +100,7 @@ extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t
   fp.v = static_cast<const uint16_t*>(v_pool);
   fp.out = out;
   fp.lse = lse;
-  if (launch_attn_fp8(fp, P->head_dim, P->n_items, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (launch_attn_fp8(fp, P->head_dim, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (launch_combine(fp, P->head_dim, false, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   return WFATTN_OK;
 }

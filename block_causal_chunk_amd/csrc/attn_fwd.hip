@@ -26,7 +26,7 @@
 namespace wfattn {
 namespace {
 
-constexpr int BM = kBlockM;  // 128 query rows per workgroup
+constexpr int BM = kBlockM;  // 256 query rows per workgroup
 constexpr int BN = kBlockN;  // 64 keys per tile
 constexpr int NTHR = 256;    // 4 waves of 64
 
@@ -34,87 +34,87 @@ constexpr int NTHR = 256;    // 4 waves of 64
 // accumulator register i of lane l holds key 16*(i/8) + 8*(l/32) + i%8 of the 32-key block.
 __device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Global -> register -> LDS staging of one key tile: K (bf16 rows of 2*D bytes, or e4m3 rows of D
-// bytes) and V (bf16).  Rows past the tile's valid keys are zero-filled, so the pool's padding
-// slots are never read.
+// Global -> LDS staging of one key tile, K (bf16 rows of 2*D bytes, or e4m3 rows of D bytes) and
+// V (bf16), with global_load_lds_dwordx4: lane i of a wave's load fills bytes [16i, 16i+16) of a
+// contiguous 1 KB run of the tile, so the swizzle is applied on the global side (the lane that
+// fills physical granule p of row r fetches logical granule p ^ f(r)).  Rows past the tile's valid
+// keys re-read the last valid row: finite data whose scores are masked to -inf and whose V rows
+// then carry weight 0, so the pool's padding slots are never read.
 template <int D, bool FP8>
 struct TileLoader {
-  static constexpr int KB = FP8 ? D : 2 * D;           // bytes per K row
-  static constexpr int KG = KB / 16;                   // 16-byte granules per K row
-  static constexpr int KPER = BN * KG / NTHR;          // K granules per thread
-  static constexpr int VPER = BN * D / 8 / NTHR;       // V granules per thread
-  uint4 kr[KPER], vr[VPER];
+  static constexpr int KB = FP8 ? D : 2 * D;    // bytes per K row
+  static constexpr int KG = KB / 16;            // 16-byte granules per K row
+  static constexpr int VG = D / 8;              // 16-byte granules per V row
+  static constexpr int KI = BN * KB / 1024 / 4; // 1 KB loads per wave for K
+  static constexpr int VI = BN * D * 2 / 1024 / 4;
 
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ k, const uint16_t* __restrict__ v, int row0,
-                                       int nvalid, int head, int H) {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int ci = threadIdx.x + NTHR * i;
-      const int row = ci / KG, g = ci % KG;
-      kr[i] = make_uint4(0, 0, 0, 0);
-      if (row < nvalid) kr[i] = *reinterpret_cast<const uint4*>(k + ((size_t)(row0 + row) * H + head) * KB + g * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int ci = threadIdx.x + NTHR * i;
-      const int row = ci / (D / 8), g = ci % (D / 8);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (row < nvalid) vr[i] = *reinterpret_cast<const uint4*>(v + ((size_t)(row0 + row) * H + head) * D + g * 8);
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* sk, uint16_t* sv) const {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int ci = threadIdx.x + NTHR * i;
-      const int row = ci / KG, g = ci % KG;
-      *reinterpret_cast<uint4*>(sk + kswz_off(row, g)) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int ci = threadIdx.x + NTHR * i;
-      const int row = ci / (D / 8), g = ci % (D / 8);
-      *reinterpret_cast<uint4*>(sv + row * D + swz<D>(row, g) * 8) = vr[i];
-    }
-  }
   // Byte offset of granule g of K row r.  bf16: the same swizzle as V.  e4m3: rows are D bytes,
   // so 256/D rows share one 64-bank line; XOR with (r / (256/D)) spreads 16 rows of one granule
   // column over distinct banks.
-  __device__ __forceinline__ static int kswz_off(int r, int g) {
-    if constexpr (FP8) return r * KB + ((g ^ ((r / (256 / D)) & (KG - 1))) * 16);
-    else return r * KB + swz<D>(r, g) * 16;
+  __device__ __forceinline__ static int kswz(int r, int g) {
+    if constexpr (FP8) return g ^ ((r / (256 / D)) & (KG - 1));
+    else return swz<D>(r, g);
+  }
+  __device__ __forceinline__ static int kswz_off(int r, int g) { return r * KB + kswz(r, g) * 16; }
+
+  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ k, const uint16_t* __restrict__ v, int row0,
+                                               int nvalid, int head, int H, uint8_t* sk, uint16_t* sv) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < KI; ++j) {
+      const int chunk = (wave * KI + j) * 64 + lane;
+      const int row = chunk / KG, g = kswz(row, chunk % KG);
+      const int src_row = row < nvalid ? row : nvalid - 1;
+      const uint8_t* src = k + ((size_t)(row0 + src_row) * H + head) * KB + g * 16;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (WF_LDS void*)(sk + (wave * KI + j) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int chunk = (wave * VI + j) * 64 + lane;
+      const int row = chunk / VG, g = swz<D>(row, chunk % VG);
+      const int src_row = row < nvalid ? row : nvalid - 1;
+      const uint16_t* src = v + ((size_t)(row0 + src_row) * H + head) * D + g * 8;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (WF_LDS void*)(reinterpret_cast<uint8_t*>(sv) + (wave * VI + j) * 1024), 16, 0, 0);
+    }
   }
 };
 
-// One work item (see the top of this file).  FP8: Q and K are e4m3 codes with one fp32 scale per
-// (64-row block, head); the product of the two block scales and the softmax scale is applied
-// once to the fp32 accumulator, P.V stays bf16.
+// Wait for this wave's outstanding global loads (the LDS fills), then the workgroup barrier.
+__device__ __forceinline__ void lds_fill_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+}
+
+// One segment: the key tiles [kt0, kt1) of one item (head, query tile of up to 256 rows).  Wave w
+// owns query rows 64w .. 64w+63 as two 32-row blocks; every K and V^T operand read from LDS feeds
+// one MFMA per block.  FP8: Q and K are e4m3 codes with one fp32 scale per (64-row block, head);
+// the product of the two block scales and the softmax scale multiplies the fp32 accumulator
+// once, and P.V stays bf16.
 template <int D, bool FP8, bool OUT_F32>
-__global__ __launch_bounds__(NTHR, 2) void attn_fwd_kernel(FwdParams p) {
+__device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* items, int item, int kt0, int kt1,
+                                            int slot, const int32_t* tiles, uint8_t* sk0, uint8_t* sk1, uint16_t* sv0,
+                                            uint16_t* sv1) {
   using Loader = TileLoader<D, FP8>;
-  constexpr int KTILE = BN * Loader::KB;  // bytes of one K tile in LDS
-  __shared__ __attribute__((aligned(16))) uint8_t smem_k[2][KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t smem_v[2][BN * D];
-  const int32_t* hdr = p.blob;
-  if (hdr[H_NONCE_LO] != (int32_t)p.nonce_lo || hdr[H_NONCE_HI] != (int32_t)p.nonce_hi) return;
-  const int32_t* it = p.blob + hdr[H_OFF_ITEMS] + (size_t)blockIdx.x * kItemInts;
-  const int head = it[0];
-  if (head < 0) return;  // idle slot of the XCD interleave
-  const int q_row0 = it[1], q_rows = it[2], kt0 = it[3], kt1 = it[4], slot = it[5], qsb = it[6];
-  const int32_t* tiles = p.blob + hdr[H_OFF_TILES];
+  const int head = ld_const(items, item * kItemInts + 0), q_row0 = ld_const(items, item * kItemInts + 1);
+  const int q_rows = ld_const(items, item * kItemInts + 2), qsb = ld_const(items, item * kItemInts + 3);
   const int H = p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int qr = wave * 32 + l32;  // this lane's query row inside the tile
-  const bool wave_active = wave * 32 < q_rows;
-  const bool ok = qr < q_rows;
+  const bool wave_active = 64 * wave < q_rows;
 
-  // Q^T as the B operand of S^T = K.Q^T.  bf16: lane holds query qr, channels 16*ks + 8*hi .. +7.
+  // Q^T as the B operand of S^T = K.Q^T.  bf16: lane holds query row r, channels 16*ks + 8*hi .. +7;
   // e4m3: channels 64*ks + 32*hi .. +31.
   constexpr int QREGS = FP8 ? D / 64 : D / 16;
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type QVec;
-  QVec qf[QREGS];
-  float c_lane = p.c;  // per-lane score multiplier: softmax scale * log2(e) [* Q block scale]
-  {
-    const size_t qoff = ((size_t)(q_row0 + (ok ? qr : 0)) * H + head) * D;
+  QVec qf[2][QREGS];
+  float cq[2];  // per-lane score multiplier: softmax scale * log2(e) [* Q block scale]
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = 64 * wave + 32 * qb + l32;
+    const bool ok = r < q_rows;
+    const size_t qoff = ((size_t)(q_row0 + (ok ? r : 0)) * H + head) * D;
 #pragma unroll
     for (int ks = 0; ks < QREGS; ++ks) {
       QVec z = {};
@@ -123,98 +123,157 @@ __global__ __launch_bounds__(NTHR, 2) void attn_fwd_kernel(FwdParams p) {
           const i32x4* src = reinterpret_cast<const i32x4*>(p.q8 + qoff + 64 * ks + 32 * hi);
           z = __builtin_shufflevector(src[0], src[1], 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        qf[ks] = z;
+        qf[qb][ks] = z;
       } else {
-        qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * hi) : z;
+        qf[qb][ks] = ok ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * hi) : z;
       }
     }
-    if constexpr (FP8) c_lane *= ok ? p.q_scale[(size_t)(qsb + qr / 64) * H + head] : 1.f;
+    cq[qb] = p.c;
+    if constexpr (FP8) cq[qb] *= ok ? p.q_scale[(size_t)(qsb + r / 64) * H + head] : 1.f;
   }
-  f32x16 o[D / 32];
+  // O lives in AGPRs (see mfma_acc_agpr); zero it, then separate the writes from the first MFMA.
+  f32x16 o[2][D / 32];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
-  // Running max m is kept in exp2 units (already multiplied by the score multiplier).
-  float m = -INFINITY, l = 0.f;
+    for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[qb][cb][i] = 0.f;
+      mfma_drain(o[qb][cb]);
+    }
+  // m: the reference max in exp2 units that P is taken against; it is raised only when a score
+  // exceeds it by more than 8 (P <= 2^8 otherwise), so O and l are rescaled rarely.  l: row sum
+  // of this lane's half of the keys.
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   const uint8_t* kbase = FP8 ? p.k8 : reinterpret_cast<const uint8_t*>(p.k);
 
-  Loader ld;
-  ld.load(kbase, p.v, tiles[2 * kt0], tiles[2 * kt0 + 1], head, H);
-  ld.store(smem_k[0], smem_v[0]);
-  __syncthreads();
+  // tile descriptors are read one tile ahead (scalar loads)
+  int cur_row0 = ld_const(tiles, 2 * kt0), cur_nv = ld_const(tiles, 2 * kt0 + 1);
+  int nxt_row0 = 0, nxt_nv = 0;
+  if (kt0 + 1 < kt1) {
+    nxt_row0 = ld_const(tiles, 2 * kt0 + 2);
+    nxt_nv = ld_const(tiles, 2 * kt0 + 3);
+  }
+  Loader::issue(kbase, p.v, cur_row0, cur_nv, head, H, sk0, sv0);
+  lds_fill_barrier();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
+  // One key tile: compute from (sk, sv) while (sk_next, sv_next) fill.  The loop below runs it
+  // with the two buffers swapped on alternate tiles, each call with distinct LDS arrays, so the
+  // compiler can see that the in-flight fill never aliases the reads of this tile.
+  auto step = [&](int kt, const uint8_t* sk, const uint16_t* sv, uint8_t* sk_next, uint16_t* sv_next) {
     const bool has_next = kt + 1 < kt1;
-    if (has_next) ld.load(kbase, p.v, tiles[2 * kt + 2], tiles[2 * kt + 3], head, H);
-    const int nvalid = tiles[2 * kt + 1];
-    float cm = c_lane;
-    if constexpr (FP8) cm *= p.k_scale[(size_t)(tiles[2 * kt] / 64) * H + head];
+    // the other buffer was last read before the previous barrier: refill it now, wait at the end
+    if (has_next) Loader::issue(kbase, p.v, nxt_row0, nxt_nv, head, H, sk_next, sv_next);
+    int n2_row0 = 0, n2_nv = 0;
+    if (kt + 2 < kt1) {
+      n2_row0 = ld_const(tiles, 2 * kt + 4);
+      n2_nv = ld_const(tiles, 2 * kt + 5);
+    }
+    const int nvalid = cur_nv;
+    float ksc = 1.f;
+    if constexpr (FP8) ksc = ld_const(p.k_scale, (cur_row0 / 64) * H + head);
     if (wave_active) {
-      const uint8_t* sk = smem_k[buf];
-      const uint16_t* sv = smem_v[buf];
-      f32x16 s[2];
+      f32x16 s[2][2];  // [query block][32-key block]
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[qb][kb][i] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
         const int krow = 32 * kb + sigma(l32);
+        if constexpr (FP8) {
+          i32x8 a[QREGS];
 #pragma unroll
-        for (int ks = 0; ks < QREGS; ++ks) {
-          if constexpr (FP8) {
+          for (int ks = 0; ks < QREGS; ++ks) {
             const int g0 = 4 * ks + 2 * hi;
             const i32x4 a0 = *reinterpret_cast<const i32x4*>(sk + Loader::kswz_off(krow, g0));
             const i32x4 a1 = *reinterpret_cast<const i32x4*>(sk + Loader::kswz_off(krow, g0 + 1));
-            const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, 0, 0, 0);
-          } else {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + Loader::kswz_off(krow, 2 * ks + hi));
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+            a[ks] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+#pragma unroll
+          for (int ks = 0; ks < QREGS; ++ks) {
+            s[0][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks], qf[0][ks], s[0][kb], 0, 0, 0, 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks], qf[1][ks], s[1][kb], 0, 0, 0, 0, 0, 0);
+          }
+        } else {
+          bf16x8 a[QREGS];
+#pragma unroll
+          for (int ks = 0; ks < QREGS; ++ks)
+            a[ks] = *reinterpret_cast<const bf16x8*>(sk + Loader::kswz_off(krow, 2 * ks + hi));
+#pragma unroll
+          for (int ks = 0; ks < QREGS; ++ks) {
+            s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[1][ks], s[1][kb], 0, 0, 0);
           }
         }
       }
       if (nvalid < BN) {  // ragged last tile of a chunk: keys past its end do not exist
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * kb + 16 * (i / 8) + 8 * hi + (i % 8) >= nvalid) s[kb][i] = -INFINITY;
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (32 * kb + 16 * (i / 8) + 8 * hi + (i % 8) >= nvalid) s[qb][kb][i] = -INFINITY;
       }
-      float mx = s[0][0];
+      float cm[2], mx[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        cm[qb] = cq[qb] * ksc;  // > 0, so scaling commutes with the max
+        // four independent max3 chains over the 32 scores, then combined
+        float a0 = max3(s[qb][0][0], s[qb][0][1], s[qb][0][2]), a1 = max3(s[qb][0][3], s[qb][0][4], s[qb][0][5]);
+        float a2 = max3(s[qb][1][0], s[qb][1][1], s[qb][1][2]), a3 = max3(s[qb][1][3], s[qb][1][4], s[qb][1][5]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = pair_max(mx) * cm;  // cm > 0, so scaling commutes with the max
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
+        for (int i = 6; i < 16; i += 2) {
+          a0 = max3(a0, s[qb][0][i], s[qb][0][i + 1]);
+          a2 = max3(a2, s[qb][1][i], s[qb][1][i + 1]);
+        }
+        a1 = max3(a1, a3, a0);
+        mx[qb] = pair_max(fmaxf(a1, a2)) * cm[qb];
+      }
+      if (__any((mx[0] > m[0] + 8.f) || (mx[1] > m[1] + 8.f))) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float m_new = fmaxf(m[qb], mx[qb]);
+          const float alpha = fast_exp2(m[qb] - m_new);
+          m[qb] = m_new;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb) {
+            mfma_drain(o[qb][cb]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[qb][cb][i] *= alpha;
+            mfma_drain(o[qb][cb]);
+          }
+        }
+      }
       // P = exp2(s * cm - m) rounded to bf16; the row sum is taken over the same rounded values
       // (v_dot2 with ones), so the weights that multiply V sum exactly to the normaliser.
-      float rs0 = 0.f, rs1 = 0.f;
-      bf16x8 pb[4];
+      bf16x8 pb[2][4];
       const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const int kb = k2 >> 1, b = 8 * (k2 & 1);
-        float e[8];
+      for (int qb = 0; qb < 2; ++qb) {
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[kb][b + j], cm, -m_new));
-        pb[k2] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-        rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[k2], pb[k2], 0, 1), ones, rs0, false);
-        rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[k2], pb[k2], 2, 3), ones, rs1, false);
-        rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[k2], pb[k2], 4, 5), ones, rs0, false);
-        rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[k2], pb[k2], 6, 7), ones, rs1, false);
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int kb = k2 >> 1, b = 8 * (k2 & 1);
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[qb][kb][b + j], cm[qb], -m[qb]));
+          pb[qb][k2] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+          rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 0, 1), ones, rs0, false);
+          rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 2, 3), ones, rs1, false);
+          rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 4, 5), ones, rs0, false);
+          rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 6, 7), ones, rs1, false);
+        }
+        l[qb] += rs0 + rs1;
       }
-      l = l * alpha + (rs0 + rs1);
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
       const int t = lane & 15, G = lane >> 4;
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb) {
+        bf16x8 a[4];
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {
           const int row = 16 * k2 + 8 * hi + (t >> 2);
@@ -223,49 +282,90 @@ __global__ __launch_bounds__(NTHR, 2) void attn_fwd_kernel(FwdParams p) {
           const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WF_LDS i16x4*)(sv + lds_off<D>(row + 4, col)));
           // whole-vector concatenation: element-wise 16-bit inserts are lowered wrongly by this
           // compiler (they reuse the first dword of each transposed read)
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[k2], o[cb], 0, 0, 0);
+          a[k2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          mfma_acc_agpr(o[0][cb], a[k2], pb[0][k2]);
+          mfma_acc_agpr(o[1][cb], a[k2], pb[1][k2]);
         }
       }
     }
-    if (has_next) ld.store(smem_k[buf ^ 1], smem_v[buf ^ 1]);
-    __syncthreads();
+    lds_fill_barrier();
+    cur_row0 = nxt_row0;
+    cur_nv = nxt_nv;
+    nxt_row0 = n2_row0;
+    nxt_nv = n2_nv;
+  };
+  int kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
+    step(kt, sk0, sv0, sk1, sv1);
+    step(kt + 1, sk1, sv1, sk0, sv0);
   }
+  if (kt < kt1) step(kt, sk0, sv0, sk1, sv1);
 
   if (!wave_active) return;
-  const float lt = pair_sum(l);
-  const float inv = 1.f / lt;
-  if (!ok) return;
-  // m is log2 of the largest exp(scale * s); lse = m * ln(2) + ln(l)
-  const float lse_val = m * 0.6931471805599453f + logf(lt);
-  if (slot < 0) {
-    const size_t rowoff = ((size_t)(q_row0 + qr) * H + head) * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+  for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * cb + 8 * g4 + 4 * hi;
-        const float v0 = o[cb][4 * g4] * inv, v1 = o[cb][4 * g4 + 1] * inv;
-        const float v2 = o[cb][4 * g4 + 2] * inv, v3 = o[cb][4 * g4 + 3] * inv;
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + rowoff + d0) = make_float4(v0, v1, v2, v3);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + rowoff + d0) =
-              make_uint2(pack2_bf16(v0, v1), pack2_bf16(v2, v3));
+    for (int cb = 0; cb < D / 32; ++cb) mfma_drain(o[qb][cb]);
+    const int r = 64 * wave + 32 * qb + l32;
+    const float lt = pair_sum(l[qb]);
+    const float inv = 1.f / lt;
+    if (r >= q_rows) continue;
+    // m is log2 of the reference exp(scale * s); lse = m * ln(2) + ln(l)
+    const float lse_val = m[qb] * 0.6931471805599453f + logf(lt);
+    if (slot < 0) {
+      const size_t rowoff = ((size_t)(q_row0 + r) * H + head) * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * cb + 8 * g4 + 4 * hi;
+          const float v0 = o[qb][cb][4 * g4] * inv, v1 = o[qb][cb][4 * g4 + 1] * inv;
+          const float v2 = o[qb][cb][4 * g4 + 2] * inv, v3 = o[qb][cb][4 * g4 + 3] * inv;
+          if constexpr (OUT_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + rowoff + d0) = make_float4(v0, v1, v2, v3);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + rowoff + d0) =
+                make_uint2(pack2_bf16(v0, v1), pack2_bf16(v2, v3));
+          }
         }
-      }
-    if (p.lse && hi == 0) p.lse[(size_t)head * p.lq + q_row0 + qr] = lse_val;
-  } else {
-    float* po = p.part_o + ((size_t)slot * BM + qr) * D;
+      if (p.lse && hi == 0) p.lse[(size_t)head * p.lq + q_row0 + r] = lse_val;
+    } else {
+      float* po = p.part_o + ((size_t)slot * BM + r) * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+      for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * cb + 8 * g4 + 4 * hi;
-        *reinterpret_cast<float4*>(po + d0) =
-            make_float4(o[cb][4 * g4] * inv, o[cb][4 * g4 + 1] * inv, o[cb][4 * g4 + 2] * inv, o[cb][4 * g4 + 3] * inv);
-      }
-    if (hi == 0) p.part_lse[(size_t)slot * BM + qr] = lse_val;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * cb + 8 * g4 + 4 * hi;
+          *reinterpret_cast<float4*>(po + d0) = make_float4(o[qb][cb][4 * g4] * inv, o[qb][cb][4 * g4 + 1] * inv,
+                                                            o[qb][cb][4 * g4 + 2] * inv, o[qb][cb][4 * g4 + 3] * inv);
+        }
+      if (hi == 0) p.part_lse[(size_t)slot * BM + r] = lse_val;
+    }
+  }
+}
+
+// Persistent workgroup: runs the segments [ranges[2w], ranges[2w+1]) of the uploaded schedule.
+template <int D, bool FP8, bool OUT_F32>
+__global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
+  using Loader = TileLoader<D, FP8>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_k0[BN * Loader::KB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem_k1[BN * Loader::KB];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_v0[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_v1[BN * D];
+  const int32_t* hdr = p.blob;
+  if (ld_const(hdr, H_NONCE_LO) != (int32_t)p.nonce_lo || ld_const(hdr, H_NONCE_HI) != (int32_t)p.nonce_hi) return;
+  const int32_t* rg = p.blob + ld_const(hdr, H_OFF_RANGES);
+  const int s0 = ld_const(rg, 2 * (int)blockIdx.x), s1 = ld_const(rg, 2 * (int)blockIdx.x + 1);
+  const int32_t* segs = p.blob + ld_const(hdr, H_OFF_SEGS);
+  const int32_t* items = p.blob + ld_const(hdr, H_OFF_ITEMS);
+  const int32_t* tiles = p.blob + ld_const(hdr, H_OFF_TILES);
+  for (int sg = s0; sg < s1; ++sg) {
+    run_segment<D, FP8, OUT_F32>(p, items, ld_const(segs, sg * kSegInts), ld_const(segs, sg * kSegInts + 1),
+                                 ld_const(segs, sg * kSegInts + 2), ld_const(segs, sg * kSegInts + 3), tiles, smem_k0, smem_k1,
+                                 smem_v0, smem_v1);
   }
 }
 
@@ -275,7 +375,8 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
   const int32_t* hdr = p.blob;
   if (hdr[H_NONCE_LO] != (int32_t)p.nonce_lo || hdr[H_NONCE_HI] != (int32_t)p.nonce_hi) return;
   const int32_t* g = p.blob + hdr[H_OFF_GROUPS] + (size_t)blockIdx.x * kGroupInts;
-  const int head = g[0], q_row0 = g[1], rows = g[2], slot0 = g[3], parts = g[4];
+  const int32_t* it = p.blob + hdr[H_OFF_ITEMS] + (size_t)g[0] * kItemInts;
+  const int head = it[0], q_row0 = it[1], rows = it[2], slot0 = g[1], parts = g[2];
   for (int idx = threadIdx.x; idx < rows * (D / 4); idx += blockDim.x) {
     const int r = idx / (D / 4), d4 = idx % (D / 4);
     float mx = -INFINITY;

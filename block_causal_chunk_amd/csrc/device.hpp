@@ -33,6 +33,14 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * D + swz<D>(r, c >> 3) * 8 + (c & 7);
 }
 
+// max of three scores in one v_max3_f32.  fmaxf would add a canonicalising v_max per operand
+// (IEEE signalling-NaN handling); scores are never NaN here.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap exchanges the upper 32 lanes of
 // its first operand with the lower 32 lanes of its second; called with x twice, one result holds
 // x of this lane and the other x of the partner lane, so the symmetric max/sum of the two results
@@ -47,6 +55,28 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// O += A.B on v_mfma_f32_32x32x16_bf16 with the accumulator pinned in AGPRs.  The attention's O
+// tile (128 fp32 per lane for two 32-row blocks at d = 128) cannot share the 256 VGPRs with Q,
+// the scores and P; held in AGPRs it is only touched by MFMAs in the key loop.  The compiler does
+// not know this instruction's latency, so every VALU access to such an accumulator must follow
+// mfma_drain() on it.
+__device__ __forceinline__ void mfma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states, ordered after the MFMAs that write `acc` and before any VALU use of it (an
+// 8-pass XDL result needs 11 before a VALU or v_accvgpr_read may touch it); also separates a
+// VALU write of `acc` from the next MFMA that reads it.
+__device__ __forceinline__ void mfma_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
+// Load through the constant address space: uniform indices become scalar loads (s_load), which
+// wait on lgkmcnt and so never stall on the vmcnt of in-flight global->LDS tile fills.
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p, int i) {
+  return ((const __attribute__((address_space(4))) T*)(p))[i];
+}
 
 // Pack 8 fp32 into bf16x8 with round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,

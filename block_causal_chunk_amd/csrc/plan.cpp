@@ -24,8 +24,11 @@ std::atomic<uint64_t> g_nonce{0x5eed0001ull};
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Item {
-  int32_t head, q_row0, rows, kt_begin, kt_end, slot, qsb, qchunk;
-  int64_t cost() const { return kt_end - kt_begin; }
+  int32_t head, q_row0, rows, qsb, qchunk, n_tiles;
+};
+
+struct Seg {
+  int32_t item, kt0, kt1, slot;
 };
 
 wfattn_status validate(const wfattn_chunk_table* t) {
@@ -71,25 +74,34 @@ wfattn_status validate(const wfattn_chunk_table* t) {
   return WFATTN_OK;
 }
 
-// Greedy list scheduling of `costs` (in launch order) onto `slots` identical slots: an estimate
-// of the makespan the hardware dispatcher reaches when it hands each next workgroup to the first
-// slot that frees up.
-int64_t makespan(const std::vector<int64_t>& costs, int slots) {
-  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> q;
-  for (int i = 0; i < slots; ++i) q.push(0);
+constexpr int kCUs = 256;      // MI355X compute units; workgroup w starts on XCD w % 8
+constexpr int kXCDs = 8;
+constexpr int kSegOverhead = 3; // a segment's Q load + epilogue, in key-tile units
+constexpr int kMinSplit = 8;    // never cut a segment shorter than this many key tiles
+
+// Longest-processing-time list scheduling of whole segments onto `bins` workgroups: returns
+// per-bin segment lists (longest first) and the makespan in key-tile units.
+int64_t lpt(const std::vector<Seg>& segs, int bins, std::vector<std::vector<int>>& out) {
+  std::vector<int> order(segs.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return segs[a].kt1 - segs[a].kt0 > segs[b].kt1 - segs[b].kt0;
+  });
+  out.assign(bins, {});
+  typedef std::pair<int64_t, int> Load;
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> q;
+  for (int b = 0; b < bins; ++b) q.push(Load(0, b));
   int64_t worst = 0;
-  for (int64_t c : costs) {
-    int64_t t = q.top() + c;
+  for (int i : order) {
+    Load l = q.top();
     q.pop();
-    q.push(t);
-    worst = std::max(worst, t);
+    l.first += segs[i].kt1 - segs[i].kt0 + kSegOverhead;
+    out[l.second].push_back(i);
+    worst = std::max(worst, l.first);
+    q.push(l);
   }
   return worst;
 }
-
-constexpr int kCUs = 256;        // MI355X compute units
-constexpr int kXCDs = 8;         // dies; workgroup i starts on XCD i % 8
-constexpr int kWgPerCU = 2;      // resident attention workgroups per CU
 
 }  // namespace
 }  // namespace wfattn
@@ -145,146 +157,160 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
     }
     P.n_tiles = static_cast<int32_t>(tiles.size() / kTileInts);
 
-    // Base items: (query chunk, query tile, head) with the whole visible prefix.
-    std::vector<Item> base;
+    // Items: (query chunk, query tile of up to kBlockM rows, head) with the whole visible prefix.
+    std::vector<Item> items;
     int64_t row0 = 0, qsb0 = 0;
     for (int i = 0; i < table->num_query_chunks; ++i) {
       const int a = table->query_chunks[i];
       const int32_t tok = table->chunk_tokens[a];
-      for (int32_t qt = 0; qt * kBlockM < tok; ++qt) {
-        const int32_t rows = std::min(kBlockM, tok - qt * kBlockM);
-        for (int32_t h = 0; h < table->num_heads; ++h)
-          base.push_back(Item{h, static_cast<int32_t>(row0 + qt * kBlockM), rows, 0, prefix_end[a],
-                              -1, static_cast<int32_t>(qsb0 + qt * (kBlockM / 64)), i});
-      }
+      for (int32_t h = 0; h < table->num_heads; ++h)
+        for (int32_t qt = 0; qt * kBlockM < tok; ++qt)
+          items.push_back(Item{h, static_cast<int32_t>(row0 + qt * kBlockM), std::min(kBlockM, tok - qt * kBlockM),
+                               static_cast<int32_t>(qsb0 + qt * (kBlockM / 64)), i, prefix_end[a]});
       row0 += tok;
       qsb0 += (tok + 63) / 64;
     }
+    // head-major order: consecutive items read the same K/V
+    std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+      return x.head != y.head ? x.head < y.head : x.q_row0 < y.q_row0;
+    });
     P.lq = row0;
     P.nqb = qsb0;
+    const int n_items = static_cast<int>(items.size());
 
-    // Split-K: explicit, or the count that minimises the estimated makespan plus merge cost.
-    const int slots = kCUs * kWgPerCU;
-    auto split_items = [&](int s) {
-      std::vector<Item> out;
-      out.reserve(base.size() * s);
-      for (const Item& it : base) {
-        const int32_t nt = it.kt_end - it.kt_begin;
-        const int parts = std::max(1, std::min<int>(s, nt));
-        for (int k = 0; k < parts; ++k) {
-          Item x = it;
-          x.kt_begin = it.kt_begin + static_cast<int32_t>(static_cast<int64_t>(nt) * k / parts);
-          x.kt_end = it.kt_begin + static_cast<int32_t>(static_cast<int64_t>(nt) * (k + 1) / parts);
-          out.push_back(x);
+    // Segments (a key range of one item) and the workgroup that runs each.
+    std::vector<Seg> segs;
+    std::vector<std::vector<int>> per_wg;  // segment indices per workgroup, in run order
+    int64_t total = 0;
+    for (const Item& it : items) total += it.n_tiles;
+    auto whole_items_lpt = [&](int parts) {
+      segs.clear();
+      for (int i = 0; i < n_items; ++i) {
+        const int32_t nt = items[i].n_tiles;
+        const int k = std::max(1, std::min(parts, nt));
+        for (int j = 0; j < k; ++j)
+          segs.push_back(Seg{i, static_cast<int32_t>(static_cast<int64_t>(nt) * j / k),
+                             static_cast<int32_t>(static_cast<int64_t>(nt) * (j + 1) / k), -1});
+      }
+      const int bins = std::min<int>(kCUs, static_cast<int>(segs.size()));
+      return lpt(segs, bins, per_wg);
+    };
+    // Stream-K: the head-major list of key tiles cut into kCUs ranges of equal cost; logical
+    // range L runs on workgroup (L / 32) + 8 * (L % 32), so the 32 workgroups of one XCD share
+    // a contiguous run of heads and hence their K/V in that XCD's L2.
+    auto stream_k = [&]() {
+      const int G = kCUs;
+      segs.clear();
+      per_wg.assign(G, {});
+      // item i owns tiles [first[i], first[i] + n_tiles) of one global axis; logical range L is
+      // [cut[L], cut[L+1]); a cut closer than kMinSplit to an item boundary snaps to it
+      std::vector<int64_t> first(n_items + 1, 0);
+      for (int i = 0; i < n_items; ++i) first[i + 1] = first[i] + items[i].n_tiles;
+      std::vector<int64_t> cut(G + 1);
+      int it_idx = 0;
+      for (int L = 0; L <= G; ++L) {
+        int64_t c = (total * L + G / 2) / G;
+        while (it_idx < n_items && first[it_idx + 1] <= c) ++it_idx;
+        if (L > 0 && L < G && it_idx < n_items) {
+          if (c - first[it_idx] < kMinSplit) c = first[it_idx];
+          else if (first[it_idx + 1] - c < kMinSplit) c = first[it_idx + 1];
+        }
+        cut[L] = (L == 0) ? 0 : std::max(c, cut[L - 1]);
+      }
+      cut[G] = total;
+      int i = 0;
+      for (int L = 0; L < G; ++L) {
+        const int w = P.xcd_remap ? (L / (G / kXCDs)) + kXCDs * (L % (G / kXCDs)) : L;
+        while (i < n_items && first[i + 1] <= cut[L]) ++i;
+        for (int j = i; j < n_items && first[j] < cut[L + 1]; ++j) {
+          const int64_t a = std::max(cut[L], first[j]), b = std::min(cut[L + 1], first[j + 1]);
+          if (b <= a) continue;
+          segs.push_back(Seg{j, static_cast<int32_t>(a - first[j]), static_cast<int32_t>(b - first[j]), -1});
+          per_wg[w].push_back(static_cast<int>(segs.size()) - 1);
         }
       }
-      return out;
+      int64_t worst = 0;
+      for (auto& v : per_wg) {
+        int64_t c = 0;
+        for (int k : v) c += segs[k].kt1 - segs[k].kt0 + kSegOverhead;
+        worst = std::max(worst, c);
+      }
+      return worst;
     };
-    auto lpt = [](std::vector<Item>& v) {
-      std::stable_sort(v.begin(), v.end(), [](const Item& a, const Item& b) { return a.cost() > b.cost(); });
-    };
-    int splits = 1;
     if (o.split_k >= 1) {
-      splits = o.split_k;
+      whole_items_lpt(o.split_k);
     } else {
-      // Each split adds a merge pass over its partial tile; price it at ~2 key tiles.
-      double best = 1e300;
-      for (int s = 1; s <= 8; ++s) {
-        std::vector<Item> v = split_items(s);
-        lpt(v);
-        std::vector<int64_t> costs;
-        costs.reserve(v.size());
-        for (auto& it : v) costs.push_back(it.cost() + 1);  // +1: per-item prologue/epilogue
-        const double est = static_cast<double>(makespan(costs, slots)) + (s > 1 ? 2.0 * s : 0.0);
-        if (est < best * 0.97) {  // prefer fewer splits unless clearly better
-          best = est;
-          splits = s;
-        }
+      // Whole items when there are enough of them to balance; else stream-K with partial merges.
+      std::vector<std::vector<int>> keep;
+      const int64_t m_lpt = whole_items_lpt(1);
+      std::vector<Seg> keep_segs = segs;
+      keep.swap(per_wg);
+      const int64_t m_sk = stream_k() + 2;  // +2: merge pass
+      if (m_lpt <= m_sk) {
+        segs.swap(keep_segs);
+        per_wg.swap(keep);
       }
     }
-    std::vector<Item> items = split_items(splits);
-    P.splits = splits;
 
-    // Partial slots and merge groups for the split items (items of one base are consecutive).
+    // Partial slots: every segment of an item that has more than one segment.
+    std::vector<int> nseg(n_items, 0);
+    for (const Seg& g : segs) ++nseg[g.item];
+    std::vector<std::vector<int>> item_segs(n_items);
+    for (int i = 0; i < static_cast<int>(segs.size()); ++i) item_segs[segs[i].item].push_back(i);
     std::vector<int32_t> groups;
-    {
-      size_t i = 0;
-      int32_t slot = 0;
-      while (i < items.size()) {
-        size_t j = i + 1;
-        while (j < items.size() && items[j].head == items[i].head && items[j].q_row0 == items[i].q_row0 &&
-               items[j].kt_begin == items[j - 1].kt_end)
-          ++j;
-        if (j - i > 1) {
-          groups.insert(groups.end(), {items[i].head, items[i].q_row0, items[i].rows, slot,
-                                       static_cast<int32_t>(j - i), 0, 0, 0});
-          for (size_t k = i; k < j; ++k) items[k].slot = slot++;
-        }
-        i = j;
-      }
-      P.n_partials = slot;
-      P.n_groups = static_cast<int32_t>(groups.size() / kGroupInts);
+    int32_t slot = 0;
+    P.max_parts = 1;
+    for (int i = 0; i < n_items; ++i) {
+      if (nseg[i] < 2) continue;
+      groups.insert(groups.end(), {i, slot, nseg[i], 0});
+      for (int sidx : item_segs[i]) segs[sidx].slot = slot++;
+      P.max_parts = std::max(P.max_parts, nseg[i]);
     }
+    P.n_partials = slot;
+    P.n_groups = static_cast<int32_t>(groups.size() / kGroupInts);
+    P.n_items = n_items;
 
-    // Launch order.  XCD-aware: split the head-major item list into 8 contiguous ranges of equal
-    // cost, one per XCD (so each XCD streams the K/V of few heads through its own L2), order each
-    // range longest-first, and interleave them so that workgroup 8*j + x is the j-th item of XCD x.
-    std::vector<Item> launch;
-    if (P.xcd_remap) {
-      std::vector<Item> hm = items;
-      std::stable_sort(hm.begin(), hm.end(), [](const Item& a, const Item& b) {
-        if (a.head != b.head) return a.head < b.head;
-        return a.q_row0 < b.q_row0;
-      });
-      int64_t total = 0;
-      for (auto& it : hm) total += it.cost() + 1;
-      std::vector<std::vector<Item>> per(kXCDs);
-      int64_t acc = 0;
-      for (auto& it : hm) {
-        int x = static_cast<int>(std::min<int64_t>(kXCDs - 1, (acc * kXCDs + (it.cost() + 1) / 2) / std::max<int64_t>(total, 1)));
-        per[x].push_back(it);
-        acc += it.cost() + 1;
-      }
-      size_t longest = 0;
-      for (auto& v : per) {
-        lpt(v);
-        longest = std::max(longest, v.size());
-      }
-      for (size_t j = 0; j < longest; ++j)
-        for (int x = 0; x < kXCDs; ++x) {
-          if (j < per[x].size()) launch.push_back(per[x][j]);
-          else launch.push_back(Item{-1, 0, 0, 0, 0, -1, 0, -1});  // idle slot keeps the stride
-        }
-      // drop trailing idle items
-      while (!launch.empty() && launch.back().head < 0) launch.pop_back();
-    } else {
-      launch = items;
-      lpt(launch);
+    // Segments in workgroup order; ranges[w] = [first, end) of workgroup w.
+    while (!per_wg.empty() && per_wg.back().empty()) per_wg.pop_back();
+    std::vector<int32_t> seg_ints, ranges;
+    for (const auto& v : per_wg) {
+      ranges.push_back(static_cast<int32_t>(seg_ints.size() / kSegInts));
+      for (int i : v) seg_ints.insert(seg_ints.end(), {segs[i].item, segs[i].kt0, segs[i].kt1, segs[i].slot});
+      ranges.push_back(static_cast<int32_t>(seg_ints.size() / kSegInts));
     }
-    P.n_items = static_cast<int32_t>(launch.size());
+    P.n_segs = static_cast<int32_t>(seg_ints.size() / kSegInts);
+    P.n_wgs = static_cast<int32_t>(per_wg.size());
 
-    // Blob: header, items, tiles, groups.
+    // Blob: header, items, segments, ranges, tiles, groups.
     P.off_items = kHeaderInts;
-    P.off_tiles = P.off_items + static_cast<size_t>(P.n_items) * kItemInts;
+    P.off_segs = P.off_items + static_cast<size_t>(n_items) * kItemInts;
+    P.off_ranges = P.off_segs + seg_ints.size();
+    P.off_tiles = P.off_ranges + ranges.size();
     P.off_groups = P.off_tiles + tiles.size();
     P.blob.assign(P.off_groups + groups.size(), 0);
-    P.blob[H_MAGIC] = static_cast<int32_t>(kMagic);
-    P.blob[H_NONCE_LO] = static_cast<int32_t>(P.nonce & 0xffffffffu);
-    P.blob[H_NONCE_HI] = static_cast<int32_t>(P.nonce >> 32);
-    P.blob[H_ITEMS] = P.n_items;
-    P.blob[H_TILES] = P.n_tiles;
-    P.blob[H_GROUPS] = P.n_groups;
-    P.blob[H_OFF_ITEMS] = static_cast<int32_t>(P.off_items);
-    P.blob[H_OFF_TILES] = static_cast<int32_t>(P.off_tiles);
-    P.blob[H_OFF_GROUPS] = static_cast<int32_t>(P.off_groups);
-    for (size_t i = 0; i < launch.size(); ++i) {
-      const Item& it = launch[i];
-      int32_t* d = &P.blob[P.off_items + i * kItemInts];
-      d[0] = it.head; d[1] = it.q_row0; d[2] = it.rows; d[3] = it.kt_begin;
-      d[4] = it.kt_end; d[5] = it.slot; d[6] = it.qsb; d[7] = it.qchunk;
+    int32_t* B = P.blob.data();
+    B[H_MAGIC] = static_cast<int32_t>(kMagic);
+    B[H_NONCE_LO] = static_cast<int32_t>(P.nonce & 0xffffffffu);
+    B[H_NONCE_HI] = static_cast<int32_t>(P.nonce >> 32);
+    B[H_ITEMS] = n_items;
+    B[H_TILES] = P.n_tiles;
+    B[H_GROUPS] = P.n_groups;
+    B[H_OFF_ITEMS] = static_cast<int32_t>(P.off_items);
+    B[H_OFF_TILES] = static_cast<int32_t>(P.off_tiles);
+    B[H_OFF_GROUPS] = static_cast<int32_t>(P.off_groups);
+    B[H_SEGS] = P.n_segs;
+    B[H_OFF_SEGS] = static_cast<int32_t>(P.off_segs);
+    B[H_WGS] = P.n_wgs;
+    B[H_OFF_RANGES] = static_cast<int32_t>(P.off_ranges);
+    for (int i = 0; i < n_items; ++i) {
+      const Item& it = items[i];
+      int32_t* d = B + P.off_items + static_cast<size_t>(i) * kItemInts;
+      d[0] = it.head; d[1] = it.q_row0; d[2] = it.rows; d[3] = it.qsb; d[4] = it.qchunk; d[5] = it.n_tiles;
     }
-    std::copy(tiles.begin(), tiles.end(), P.blob.begin() + P.off_tiles);
-    std::copy(groups.begin(), groups.end(), P.blob.begin() + P.off_groups);
+    std::copy(seg_ints.begin(), seg_ints.end(), B + P.off_segs);
+    std::copy(ranges.begin(), ranges.end(), B + P.off_ranges);
+    std::copy(tiles.begin(), tiles.end(), B + P.off_tiles);
+    std::copy(groups.begin(), groups.end(), B + P.off_groups);
 
     // Workspace layout.
     const size_t D = static_cast<size_t>(P.head_dim);
@@ -347,8 +373,8 @@ extern "C" wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t
   size_t total = 0;
   switch (what) {
     case 0:
-      tmp = {P->n_items, P->n_tiles, P->n_groups, P->n_partials, P->block_m, P->block_n, P->splits,
-             P->num_query_chunks};
+      tmp = {P->n_items, P->n_tiles, P->n_groups, P->n_partials, P->block_m, P->block_n, P->max_parts,
+             P->num_query_chunks, P->n_segs, P->n_wgs};
       src = tmp.data();
       total = tmp.size();
       break;
@@ -363,6 +389,14 @@ extern "C" wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t
     case 3:
       src = P->blob.data() + P->off_groups;
       total = static_cast<size_t>(P->n_groups) * kGroupInts;
+      break;
+    case 4:
+      src = P->blob.data() + P->off_segs;
+      total = static_cast<size_t>(P->n_segs) * kSegInts;
+      break;
+    case 5:
+      src = P->blob.data() + P->off_ranges;
+      total = static_cast<size_t>(P->n_wgs) * kRangeInts;
       break;
     default:
       return WFATTN_ERR_INVALID;

@@ -9,14 +9,17 @@
 
 namespace wfattn {
 
-// Tile geometry of the attention kernels (rows of Q per workgroup, keys per LDS tile).
-constexpr int kBlockM = 128;
+// Tile geometry of the attention kernels: 256 query rows per workgroup (4 waves x 64 rows),
+// 64 keys per LDS tile.
+constexpr int kBlockM = 256;
 constexpr int kBlockN = 64;
 constexpr int kItemInts = 8;   // ints per work item
+constexpr int kSegInts = 4;    // ints per segment
+constexpr int kRangeInts = 2;  // ints per workgroup range
 constexpr int kTileInts = 2;   // ints per key tile
-constexpr int kGroupInts = 8;  // ints per combine group
+constexpr int kGroupInts = 4;  // ints per merge group
 constexpr int kHeaderInts = 16;
-constexpr uint32_t kMagic = 0x57464131u;  // "WFA1"
+constexpr uint32_t kMagic = 0x57464132u;  // "WFA2"
 
 // Header words of the uploaded blob (int32 index).
 enum HeaderWord {
@@ -29,6 +32,10 @@ enum HeaderWord {
   H_OFF_ITEMS = 6,
   H_OFF_TILES = 7,
   H_OFF_GROUPS = 8,
+  H_SEGS = 9,
+  H_OFF_SEGS = 10,
+  H_WGS = 11,
+  H_OFF_RANGES = 12,
 };
 
 struct Plan {
@@ -42,10 +49,10 @@ struct Plan {
   int64_t pool_rows = 0;    // num_pages * page_size
   float scale = 0.f;        // resolved softmax scale
   // schedule
-  int32_t block_m = kBlockM, block_n = kBlockN, splits = 1, xcd_remap = 1;
-  int32_t n_items = 0, n_tiles = 0, n_groups = 0, n_partials = 0;
-  std::vector<int32_t> blob;  // header + items + key tiles + combine groups, uploaded verbatim
-  size_t off_items = 0, off_tiles = 0, off_groups = 0;  // int32 offsets into blob
+  int32_t block_m = kBlockM, block_n = kBlockN, max_parts = 1, xcd_remap = 1;
+  int32_t n_items = 0, n_tiles = 0, n_groups = 0, n_partials = 0, n_segs = 0, n_wgs = 0;
+  std::vector<int32_t> blob;  // header, items, segments, ranges, key tiles, merge groups
+  size_t off_items = 0, off_segs = 0, off_ranges = 0, off_tiles = 0, off_groups = 0;  // int32 offsets
   // workspace layout (bytes)
   size_t ws_blob = 0, ws_part_o = 0, ws_part_lse = 0, ws_stage = 0;
   size_t ws_base_bytes = 0;   // blob + partials

@@ -95,8 +95,10 @@ typedef struct wfattn_chunk_table {
 
 /* Planner options; zero-initialise for defaults. */
 typedef struct wfattn_opts {
-  int32_t split_k;   /* 0: the planner decides; 1: never split a query tile's keys; n > 1: split */
-                     /* every query tile's key range into up to n parts merged through the LSE   */
+  int32_t split_k;   /* 0: the planner decides (whole items, or equal-cost ranges per workgroup */
+                     /* cut across items when that balances better); 1: never cut an item's key */
+                     /* range; n > 1: cut every item's key range into up to n parts; parts are  */
+                     /* merged through their LSEs                                                */
   int32_t xcd_remap; /* 0: default (on); 1: on; -1: off.  Groups one head's work on one XCD     */
   int32_t reserved0; /* must be 0 */
   int32_t reserved1; /* must be 0 */
@@ -127,13 +129,21 @@ size_t wfattn_workspace_bytes(const wfattn_plan_t* plan, int32_t mode);
 wfattn_status wfattn_plan_upload(const wfattn_plan_t* plan, void* ws, size_t ws_bytes,
                                  void* stream);
 
-/* Introspection for host tests.  what = 0: summary, 8 int32 (items, key tiles, combine groups,
- * partial slots, block_m, block_n, splits used, query chunks); what = 1: work items, 8 int32
- * each (head, first Q row, rows, first key tile, end key tile, partial slot or -1, first Q-scale
- * block, query chunk index) in launch order; what = 2: key tiles, 2 int32 each (first pool row,
- * valid keys); what = 3: combine groups, 8 int32 each (head, first Q row, rows, first partial
- * slot, parts, 0, 0, 0).  Copies min(cap, total) int32 into buf (buf may be NULL when cap == 0)
- * and stores the total count of int32 in *n. */
+/* Introspection for host tests.  The schedule is a list of items -- (head, query tile of up to
+ * 256 rows of one query chunk) with that chunk's whole visible key-tile prefix -- cut into
+ * segments (a key-tile range of one item), which the persistent workgroups run in order; items
+ * cut into several segments are merged through their LSEs afterwards.
+ * what = 0: summary, 10 int32 (items, key tiles, merge groups, partial slots, block_m, block_n,
+ *           most segments of one item, query chunks, segments, workgroups);
+ * what = 1: items, 8 int32 each (head, first Q row, rows, first Q-scale block, query chunk
+ *           index, visible key tiles, 0, 0);
+ * what = 2: key tiles in clean -> noisy order, 2 int32 each (first pool row, valid keys);
+ * what = 3: merge groups, 4 int32 each (item, first partial slot, parts, 0);
+ * what = 4: segments in workgroup order, 4 int32 each (item, first key tile, end key tile,
+ *           partial slot or -1);
+ * what = 5: workgroups, 2 int32 each (first segment, end segment).
+ * Copies min(cap, total) int32 into buf (buf may be NULL when cap == 0) and stores the total
+ * count of int32 in *n.  Errors: NULL, INVALID (bad plan or unknown `what`). */
 wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t what, int32_t* buf,
                                    size_t cap, size_t* n);
 

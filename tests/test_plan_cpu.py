@@ -140,31 +140,63 @@ def _owner_of_pool_row(t):
     return own
 
 
+def _check_tiles_vectorized(t, items, tiles, own, bm, bn):
+    """Tile-level form of the exhaustive check for big tables: each key tile lies in one page of
+    one chunk, the tiles of the clean -> noisy prefix of query chunk a cover exactly the tokens of
+    the chunks visible to a, each once."""
+    tile_chunk = np.empty(len(tiles), np.int64)
+    for k, (row0, nv) in enumerate(tiles):
+        b0, u0 = own[int(row0)]
+        b1, u1 = own[int(row0) + int(nv) - 1]
+        assert b0 == b1 and u1 == u0 + nv - 1
+        tile_chunk[k] = b0
+    for head, r0, rows, qsb, qi, nt, _, _ in items:
+        a = int(t.query_chunks[qi])
+        ch = tile_chunk[:nt]
+        assert (t.chunk_order[ch] <= t.chunk_order[a]).all()
+        vis = [b for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a]]
+        assert int(tiles[:nt, 1].sum()) == sum(int(t.chunk_tokens[b]) for b in vis)
+        assert set(ch.tolist()) == set(vis)
+
+
 def _check_schedule(B, t, **kw):
     plan = B.wfattn_plan(t, **kw)
-    summ = plan.describe(0)
-    n_items, n_tiles, n_groups, n_parts, bm, bn = [int(x) for x in summ[:6]]
+    summ = [int(x) for x in plan.describe(0)]
+    n_items, n_tiles, n_groups, n_parts, bm, bn, max_parts, nqc, n_segs, n_wgs = summ
     items = plan.describe(1).reshape(-1, 8)
     tiles = plan.describe(2).reshape(-1, 2)
-    groups = plan.describe(3).reshape(-1, 8)
+    groups = plan.describe(3).reshape(-1, 4)
+    segs = plan.describe(4).reshape(-1, 4)
+    ranges = plan.describe(5).reshape(-1, 2)
     assert items.shape[0] == n_items and tiles.shape[0] == n_tiles and groups.shape[0] == n_groups
+    assert segs.shape[0] == n_segs and ranges.shape[0] == n_wgs and 1 <= n_wgs <= 256
+    # workgroup ranges partition the segment list in order
+    assert ranges[0, 0] == 0 and ranges[-1, 1] == n_segs
+    assert (ranges[1:, 0] == ranges[:-1, 1]).all() and (ranges[:, 1] >= ranges[:, 0]).all()
     own = _owner_of_pool_row(t)
-    # query row -> query chunk
     qstart = np.concatenate([[0], np.cumsum([int(t.chunk_tokens[a]) for a in t.query_chunks])])
-    seen = {}
-    slots = set()
-    for head, r0, rows, k0, k1, slot, qsb, qi in items:
-        if head < 0:
-            assert k0 == k1 == 0
-            continue
-        assert 0 <= head < t.num_heads and 1 <= rows <= bm and 0 <= k0 < k1 <= n_tiles
+    for head, r0, rows, qsb, qi, nt, _, _ in items:
+        assert 0 <= head < t.num_heads and 1 <= rows <= bm and 1 <= nt <= n_tiles
         assert qstart[qi] <= r0 and r0 + rows <= qstart[qi + 1]  # a query tile never crosses a chunk
         assert (r0 - qstart[qi]) % bm == 0
-        a = int(t.query_chunks[qi])
+    # the segments of each item cover its key tiles exactly once
+    cover = [np.zeros(int(it[5]), np.int32) for it in items]
+    slots = {}
+    for item, k0, k1, slot in segs:
+        assert 0 <= k0 < k1 <= items[item][5]
+        cover[item][k0:k1] += 1
         if slot >= 0:
             assert slot not in slots
-            slots.add(slot)
-        for kt in range(k0, k1):
+            slots[int(slot)] = int(item)
+    assert all((c == 1).all() for c in cover)
+    n_pairs = sum(int(it[5]) for it in items) * bn
+    if n_pairs > 2_000_000:
+        _check_tiles_vectorized(t, items, tiles, own, bm, bn)
+        return plan, items, tiles
+    seen = {}
+    for i, (head, r0, rows, qsb, qi, nt, _, _) in enumerate(items):
+        a = int(t.query_chunks[qi])
+        for kt in range(nt):
             row0, nv = tiles[kt]
             assert 1 <= nv <= bn
             b0, u0 = own[int(row0)]
@@ -175,7 +207,6 @@ def _check_schedule(B, t, **kw):
                 key = (int(head), int(r0), b, u)
                 assert key not in seen  # exactly once
                 seen[key] = True
-    # every visible (head, query tile, key) appears
     expect = 0
     for qi, a in enumerate(t.query_chunks):
         vis = sum(int(t.chunk_tokens[b]) for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a])
@@ -183,12 +214,12 @@ def _check_schedule(B, t, **kw):
         expect += vis * n_qt * t.num_heads
     assert len(seen) == expect
     assert len(slots) == n_parts
-    # merge groups cover exactly the split items
-    gsl = set()
-    for head, r0, rows, s0, parts, *_ in groups:
-        assert parts >= 2
-        gsl.update(range(s0, s0 + parts))
-    assert gsl == slots
+    # merge groups: exactly the items with more than one segment, slots contiguous per item
+    nseg = np.bincount(segs[:, 0], minlength=n_items)
+    assert set(int(g[0]) for g in groups) == set(int(i) for i in np.nonzero(nseg > 1)[0])
+    for item, s0, parts, _ in groups:
+        assert parts == nseg[item] and parts <= max_parts
+        assert all(slots[s] == item for s in range(s0, s0 + parts))
     return plan, items, tiles
 
 
@@ -212,24 +243,26 @@ def test_schedule_random_tables(B):
 
 
 def test_schedule_full_size_tables_and_xcd_grouping(B):
-    """The five workloads' tables (sizes only; no values are drawn)."""
+    """The five workloads' tables (sizes only; no values are drawn): coverage, balance across
+    the 256 workgroups and the 8 XCDs, and few heads per XCD."""
     from block_causal_chunk_amd.inputs import WORKLOADS
     for name, w in WORKLOADS.items():
         t = make_table(w["tokens"], list(range(len(w["tokens"]))), w["queries"], w["page"], w["H"], w["d"],
                        shuffle_rng=np.random.default_rng(0), spare=w["spare"])
-        plan = B.wfattn_plan(t)
-        items = plan.describe(1).reshape(-1, 8)
-        cost = np.zeros(8)
-        heads = [set() for _ in range(8)]
-        for i, it in enumerate(items):
-            if it[0] >= 0:
-                cost[i % 8] += it[4] - it[3] + 1
-                heads[i % 8].add(int(it[0]))
-        assert cost.max() <= 1.15 * cost.mean() + 64, (name, cost)
+        plan, items, tiles = _check_schedule(B, t)
+        segs = plan.describe(4).reshape(-1, 4)
+        ranges = plan.describe(5).reshape(-1, 2)
+        load = np.array([sum(int(segs[s][2] - segs[s][1]) + 3 for s in range(a, b)) for a, b in ranges])
         if name != "tiny_fp32":
-            # each XCD streams the K/V of few heads
+            assert load.max() <= 1.12 * load.mean() + 16, (name, load.max(), load.mean())
+            xcd = np.zeros(8)
+            heads = [set() for _ in range(8)]
+            for wg, (a, b) in enumerate(ranges):
+                for sidx in range(a, b):
+                    xcd[wg % 8] += segs[sidx][2] - segs[sidx][1]
+                    heads[wg % 8].add(int(items[segs[sidx][0]][0]))
+            assert xcd.max() <= 1.15 * xcd.mean(), (name, xcd)
             assert max(len(h) for h in heads) <= -(-w["H"] // 8) + 2, (name, heads)
-    # sizes of the workload tables
     t = make_table([4680] * 4, [0, 1, 2, 3], [3], 256, 12, 128)
     tiles = B.wfattn_plan(t, split_k=1).describe(2).reshape(-1, 2)
     assert tiles.shape[0] == 4 * (18 * 4 + 2) and tiles[:, 1].sum() == 4 * 4680
