@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--cold", action="store_true", help="evict the 256 MB Infinity Cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 256 MiB device copy (3 times) so that a "
+                         "counter run can scale FETCH_SIZE/WRITE_SIZE against known bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (no collectives, no sharding); "
@@ -171,6 +174,13 @@ def main():
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
     ms = float(per.mean())
     flops = effective_flops(t)

@@ -30,6 +30,10 @@ def common_flags():
             # keep MFMA accumulators in VGPRs: with AGPR-form accumulators the allocator moves the
             # O tile between AGPRs and VGPRs around every MFMA group of the attention loop
             "-mllvm", "-amdgpu-mfma-vgpr-form=true",
+            # keep the two specialisations of the attention tile's front half apart: sinking their
+            # common tail into the join block would separate the exponentials from the MFMAs they
+            # are meant to overlap
+            "-mllvm", "-simplifycfg-sink-common=false",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

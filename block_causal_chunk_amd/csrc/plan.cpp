@@ -192,7 +192,19 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
           segs.push_back(Seg{i, static_cast<int32_t>(static_cast<int64_t>(nt) * j / k),
                              static_cast<int32_t>(static_cast<int64_t>(nt) * (j + 1) / k), -1});
       }
-      const int bins = std::min<int>(kCUs, static_cast<int>(segs.size()));
+      const int n_segs = static_cast<int>(segs.size());
+      if (n_segs <= kCUs && P.xcd_remap) {
+        // one segment per workgroup: the head-major segment list laid out XCD by XCD, so the
+        // workgroups of one XCD walk the same heads' keys side by side and share them in L2
+        per_wg.assign(kCUs, {});
+        int64_t worst = 0;
+        for (int L = 0; L < n_segs; ++L) {
+          per_wg[(L / (kCUs / kXCDs)) + kXCDs * (L % (kCUs / kXCDs))].push_back(L);
+          worst = std::max<int64_t>(worst, segs[L].kt1 - segs[L].kt0 + kSegOverhead);
+        }
+        return worst;
+      }
+      const int bins = std::min<int>(kCUs, n_segs);
       return lpt(segs, bins, per_wg);
     };
     // Stream-K: the head-major list of key tiles cut into kCUs ranges of equal cost; logical
