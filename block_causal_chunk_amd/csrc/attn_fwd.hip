@@ -1,22 +1,26 @@
 // attn_fwd.hip -- block-causal chunk attention forward, bf16 MFMA (gfx950).
 //
-// What one workgroup computes: one work item = (head, query tile of up to 128 rows of one query
-// chunk, a contiguous range of that chunk's visible key tiles).  The visible keys are the chunk's
+// What one workgroup computes: segments of work items, one item = (head, query tile of up to
+// 256 rows of one query chunk, that chunk's visible key tiles).  The visible keys are the chunk's
 // own tokens and every earlier, cleaner chunk's tokens (Wave Forcing project page, "01 - The
 // design gap", directed frontier and "Key observation"); the planner has already reduced them to
 // a list of 64-key tiles that never cross a page, so nothing here tests chunk visibility: masked
 // tiles are simply not in the list.  Keys are read from the paged pool in place (project page,
 // "03 - End-to-end KV transport", "Layout" panel).
 //
-// Data flow per key tile (4 waves, 32 query rows each):
-//   K, V tile [64 x d] : global (16 B per lane, coalesced rows) -> registers -> swizzled LDS,
-//                        double-buffered so the next tile's loads fly during this tile's math
-//   S^T = K . Q^T      : v_mfma_f32_32x32x16_bf16, K rows read from LDS in a bit-swapped order
-//                        so each lane ends up owning 8 consecutive keys of one query
-//   online softmax     : fp32 in registers; one lane pair (l, l^32) per query, exp2 with the
-//                        softmax scale folded into log2(e)
-//   O^T += V^T . P^T   : P stays in registers as the B operand; V^T comes from LDS through
-//                        ds_read_b64_tr_b16 transposed reads
+// Data flow (4 waves, 64 query rows each, as two 32-row MFMA blocks):
+//   K, V tiles [64 x d] : global -> LDS with global_load_lds_dwordx4, a ring of three buffers
+//                         filled two tiles ahead of their use
+//   S^T = K . Q^T       : v_mfma_f32_32x32x16_bf16, K rows read from LDS in a bit-swapped order
+//                         so each lane ends up owning 16 keys of one query
+//   softmax             : P = exp2(S * c - m) in fp32 against a fixed per-row reference m
+//   O^T += V^T . P^T    : P stays in registers as the B operand; V^T comes from LDS through
+//                         ds_read_b64_tr_b16 transposed reads; O lives in AGPRs
+//
+// The key loop is software-pipelined in half tiles (32 keys).  One half step issues the score
+// MFMAs of the next half and the P.V MFMAs of the previous half, one at a time, and between two
+// MFMAs a few of the VALU operations that turn the current half's scores into P, so the matrix
+// cores and the VALU work at the same time within the single wave of each SIMD.
 #include <type_traits>
 
 #include "device.hpp"
@@ -29,17 +33,34 @@ namespace {
 constexpr int BM = kBlockM;  // 256 query rows per workgroup
 constexpr int BN = kBlockN;  // 64 keys per tile
 constexpr int NTHR = 256;    // 4 waves of 64
+constexpr int NBUF = 3;      // LDS ring depth (tiles)
 
 // Row of the K tile that lane row r of the S^T A-operand reads: bits 2 and 3 swapped.  With it,
 // accumulator register i of lane l holds key 16*(i/8) + 8*(l/32) + i%8 of the 32-key block.
 __device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Calls f(integral_constant<int, i>) for i = B .. E-1, so that i is a constant expression.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Global -> LDS staging of one key tile, K (bf16 rows of 2*D bytes, or e4m3 rows of D bytes) and
 // V (bf16), with global_load_lds_dwordx4: lane i of a wave's load fills bytes [16i, 16i+16) of a
 // contiguous 1 KB run of the tile, so the swizzle is applied on the global side (the lane that
-// fills physical granule p of row r fetches logical granule p ^ f(r)).  Rows past the tile's valid
-// keys re-read the last valid row: finite data whose scores are masked to -inf and whose V rows
-// then carry weight 0, so the pool's padding slots are never read.
+// fills physical granule p of row r fetches logical granule p ^ f(r)).  The per-lane byte offsets
+// relative to the tile's first pool row are fixed for a segment, so a fill is one scalar base
+// address and one precomputed VGPR offset per load.  Rows past the tile's valid keys re-read the
+// last valid row: finite data whose scores are masked to -inf and whose V rows then carry weight
+// 0, so the pool's padding slots are never read.
 template <int D, bool FP8>
 struct TileLoader {
   static constexpr int KB = FP8 ? D : 2 * D;    // bytes per K row
@@ -47,6 +68,8 @@ struct TileLoader {
   static constexpr int VG = D / 8;              // 16-byte granules per V row
   static constexpr int KI = BN * KB / 1024 / 4; // 1 KB loads per wave for K
   static constexpr int VI = BN * D * 2 / 1024 / 4;
+
+  uint32_t koff[KI], voff[VI];
 
   // Byte offset of granule g of K row r.  bf16: the same swizzle as V.  e4m3: rows are D bytes,
   // so 256/D rows share one 64-bank line; XOR with (r / (256/D)) spreads 16 rows of one granule
@@ -57,38 +80,100 @@ struct TileLoader {
   }
   __device__ __forceinline__ static int kswz_off(int r, int g) { return r * KB + kswz(r, g) * 16; }
 
-  // The fills are written as inline asm so that the compiler does not treat them as LDS stores:
-  // it would otherwise wait for every in-flight fill (of the other buffer) before each LDS read
-  // of this tile.  Completion is awaited explicitly by lds_fill_barrier().  M0 carries the LDS
-  // destination of global_load_lds; nothing else in these kernels uses M0.
-  __device__ __forceinline__ static void dma16(const void* src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory");
+  __device__ __forceinline__ static uint32_t k_src(int wave, int j, int lane, int nvalid, int head, int H) {
+    const int chunk = (wave * KI + j) * 64 + lane;
+    const int row = chunk / KG, g = kswz(row, chunk % KG);
+    const int src = row < nvalid ? row : nvalid - 1;
+    return (uint32_t)((src * H + head) * KB + g * 16);
   }
-  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ k, const uint16_t* __restrict__ v, int row0,
-                                               int nvalid, int head, int H, uint32_t sk, uint32_t sv) {
+  __device__ __forceinline__ static uint32_t v_src(int wave, int j, int lane, int nvalid, int head, int H) {
+    const int chunk = (wave * VI + j) * 64 + lane;
+    const int row = chunk / VG, g = swz<D>(row, chunk % VG);
+    const int src = row < nvalid ? row : nvalid - 1;
+    return (uint32_t)((src * H + head) * 2 * D + g * 16);
+  }
+
+  __device__ __forceinline__ void init(int head, int H) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < KI; ++j) koff[j] = k_src(wave, j, lane, BN, head, H);
+#pragma unroll
+    for (int j = 0; j < VI; ++j) voff[j] = v_src(wave, j, lane, BN, head, H);
+  }
+
+  // The fills are inline asm so that the compiler does not treat them as LDS stores: it would
+  // otherwise wait for every in-flight fill before each LDS read.  Completion is awaited with
+  // explicit vmcnt waits.  M0 carries the LDS destination of global_load_lds; nothing else in
+  // these kernels uses M0.
+  __device__ __forceinline__ static void dma16(uint32_t lds_addr, uint32_t off, const uint8_t* base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(off), "s"(base) : "memory");
+  }
+  // K of the tile whose first key is pool row row0, into the LDS buffer at byte address lds.
+  __device__ __forceinline__ void fill_k(const uint8_t* kpool, int row0, int nvalid, int head, int H, uint32_t lds) const {
+    const uint8_t* base = kpool + (size_t)row0 * H * KB;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    if (nvalid == BN) {
 #pragma unroll
-    for (int j = 0; j < KI; ++j) {
-      const int chunk = (wave * KI + j) * 64 + lane;
-      const int row = chunk / KG, g = kswz(row, chunk % KG);
-      const int src_row = row < nvalid ? row : nvalid - 1;
-      dma16(k + ((size_t)(row0 + src_row) * H + head) * KB + g * 16, __builtin_amdgcn_readfirstlane(sk + (wave * KI + j) * 1024));
+      for (int j = 0; j < KI; ++j) dma16(lds + (wave * KI + j) * 1024, koff[j], base);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KI; ++j)
+        dma16(lds + (wave * KI + j) * 1024, k_src(wave, j, threadIdx.x & 63, nvalid, head, H), base);
     }
+  }
+  __device__ __forceinline__ void fill_v(const uint8_t* vpool, int row0, int nvalid, int head, int H, uint32_t lds) const {
+    const uint8_t* base = vpool + (size_t)row0 * H * 2 * D;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (nvalid == BN) {
 #pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const int chunk = (wave * VI + j) * 64 + lane;
-      const int row = chunk / VG, g = swz<D>(row, chunk % VG);
-      const int src_row = row < nvalid ? row : nvalid - 1;
-      dma16(v + ((size_t)(row0 + src_row) * H + head) * D + g * 8, __builtin_amdgcn_readfirstlane(sv + (wave * VI + j) * 1024));
+      for (int j = 0; j < VI; ++j) dma16(lds + (wave * VI + j) * 1024, voff[j], base);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VI; ++j)
+        dma16(lds + (wave * VI + j) * 1024, v_src(wave, j, threadIdx.x & 63, nvalid, head, H), base);
     }
   }
 };
 
-// Wait for this wave's outstanding global loads (the LDS fills), then the workgroup barrier.
-__device__ __forceinline__ void lds_fill_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+// The VALU work that turns 32 scores per lane (2 query blocks x 16 keys) into bf16 P and the row
+// sums, as 96 operations in a software-pipelined order: for element e, F(e) = fma(s, c, -m),
+// X(e) = exp2, then per pair of elements C = convert to bf16x2 and D = add to the row sum.  Each
+// operation depends only on operations at least two places earlier in the list, so any run of
+// consecutive operations can be issued between two MFMAs without waiting on each other.
+enum : int { OP_F = 0, OP_X = 1, OP_C = 2, OP_D = 3 };
+struct ValuProgram {
+  int kind[96], idx[96];
+  constexpr ValuProgram() : kind(), idx() {
+    int n = 0;
+    for (int s = 0; s < 36; ++s) {
+      if (s < 32) { kind[n] = OP_F; idx[n] = s; ++n; }
+      if (s >= 1 && s <= 32) { kind[n] = OP_X; idx[n] = s - 1; ++n; }
+      if (s >= 3 && (s & 1) && (s - 3) / 2 < 16) { kind[n] = OP_C; idx[n] = (s - 3) / 2; ++n; }
+      if (s >= 4 && !(s & 1) && (s - 4) / 2 < 16) { kind[n] = OP_D; idx[n] = (s - 4) / 2; ++n; }
+    }
+  }
+};
+constexpr ValuProgram kValu{};
+
+// Order of the MFMAs inside a half step: NS score MFMAs spread evenly among NP P.V MFMAs.
+__host__ __device__ constexpr bool region_is_s(int r, int ns, int np) {
+  return ns > 0 && ((r + 1) * ns) / (ns + np) > (r * ns) / (ns + np);
+}
+__host__ __device__ constexpr int region_index(int r, int ns, int np) {  // index among its own kind
+  int k = 0;
+  for (int i = 0; i < r; ++i) k += region_is_s(i, ns, np) == region_is_s(r, ns, np);
+  return k;
+}
+// first region that uses K operand ks (score MFMA 2*ks) or V operand t (P.V MFMA 2*t)
+__host__ __device__ constexpr int k_first_use(int ks, int ns, int np) {
+  for (int r = 0; r < ns + np; ++r)
+    if (region_is_s(r, ns, np) && region_index(r, ns, np) == 2 * ks) return r;
+  return 0;
+}
+__host__ __device__ constexpr int v_first_use(int t, int ns, int np) {
+  for (int r = 0; r < ns + np; ++r)
+    if (!region_is_s(r, ns, np) && region_index(r, ns, np) == 2 * t) return r;
+  return 0;
 }
 
 // One segment: the key tiles [kt0, kt1) of one item (head, query tile of up to 256 rows).  Wave w
@@ -98,24 +183,29 @@ __device__ __forceinline__ void lds_fill_barrier() {
 // once, and P.V stays bf16.
 //
 // Softmax reference.  P = exp2(s*c - m) against a per-row reference m in exp2 units, fixed from
-// the first tile of the segment (that tile computes its max before its exponentials).  Later
-// tiles therefore need no max before P, so their exponentials overlap the score MFMAs, and O is
-// never rescaled inside the key loop.  Any reference works as long as no P overflows: the true
-// running max is tracked, and if some score exceeded m by more than 2^64 (P could have
-// overflowed, which needs scores to jump by more than 44 natural-log units after the first
-// tile) the whole segment is recomputed with m set to that max, which no score exceeds.
+// the first tile of the segment, so O is never rescaled inside the key loop and no running max is
+// kept.  Any reference gives the exact softmax as long as no P overflows.  The row sum l bounds
+// every P of the row; if some l reaches 2^64 (some score exceeded the first tile's max by more
+// than 44 natural-log units) the segment is recomputed against the true row max, found by a
+// score-only sweep, which no score exceeds.
 template <int D, bool FP8, bool OUT_F32>
 __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* items, int item, int kt0, int kt1,
                                             int slot, const int32_t* tiles,
                                             uint8_t (*smem_k)[BN * TileLoader<D, FP8>::KB], uint16_t (*smem_v)[BN * D],
                                             int* redo_flags) {
   using Loader = TileLoader<D, FP8>;
+  constexpr int KI = Loader::KI, VI = Loader::VI;
   const int head = ld_const(items, item * kItemInts + 0), q_row0 = ld_const(items, item * kItemInts + 1);
   const int q_rows = ld_const(items, item * kItemInts + 2), qsb = ld_const(items, item * kItemInts + 3);
   const int H = p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const bool wave_active = 64 * wave < q_rows;
+  const int n = kt1 - kt0;
 
+  Loader ld;
+  ld.init(head, H);
+  const uint8_t* kpool = FP8 ? p.k8 : reinterpret_cast<const uint8_t*>(p.k);
+  const uint8_t* vpool = reinterpret_cast<const uint8_t*>(p.v);
   // Q^T as the B operand of S^T = K.Q^T.  bf16: lane holds query row r, channels 16*ks + 8*hi .. +7;
   // e4m3: channels 64*ks + 32*hi .. +31.
   constexpr int QREGS = FP8 ? D / 64 : D / 16;
@@ -143,191 +233,60 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     cq[qb] = p.c;
     if constexpr (FP8) cq[qb] *= ok ? p.q_scale[(size_t)(qsb + r / 64) * H + head] : 1.f;
   }
-  const uint8_t* kbase = FP8 ? p.k8 : reinterpret_cast<const uint8_t*>(p.k);
+  // Q^T lives in AGPRs for the whole segment (read only by the score MFMAs)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
 
+  // ---- operands ------------------------------------------------------------------------------
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type KVec;
+  // K operand of score k-step ks for the 32 keys of half kb
+  auto k_op = [&](const uint8_t* sk, int kb, int ks) -> KVec {
+    const int krow = 32 * kb + sigma(l32);
+    if constexpr (FP8) {
+      const int g0 = 4 * ks + 2 * hi;
+      const i32x4 a0 = *reinterpret_cast<const i32x4*>(sk + Loader::kswz_off(krow, g0));
+      const i32x4 a1 = *reinterpret_cast<const i32x4*>(sk + Loader::kswz_off(krow, g0 + 1));
+      return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(sk + Loader::kswz_off(krow, 2 * ks + hi));
+    }
+  };
+  // V^T operand of (d block cb, 16-key step k2 of the tile) through two transposed LDS reads
+  const int tq = lane & 15, G = lane >> 4;
+  auto v_op = [&](const uint16_t* sv, int cb, int k2) -> bf16x8 {
+    const int row = 16 * k2 + 8 * hi + (tq >> 2);
+    const int col = 32 * cb + 16 * (G & 1) + 4 * (tq & 3);
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WF_LDS i16x4*)(sv + lds_off<D>(row, col)));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WF_LDS i16x4*)(sv + lds_off<D>(row + 4, col)));
+    // whole-vector concatenation: element-wise 16-bit inserts are lowered wrongly by this
+    // compiler (they reuse the first dword of each transposed read)
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // Score MFMAs are inline asm so that Q^T can stay in AGPRs as their B operand (the builtins
+  // would copy it into VGPRs, which the two score halves, P and the operands need).  The compiler
+  // does not track their latency: every VALU read of a score follows score_drain() or enough
+  // independent instructions (the pipelined loop reads a half's scores one half step later).
+  auto s_mfma = [&](f32x16& acc, const KVec& a, int qb, int ks, auto firstc) {
+    if constexpr (decltype(firstc)::value) {
+      if constexpr (FP8) asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(qf[qb][ks]));
+      else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(qf[qb][ks]));
+    } else {
+      if constexpr (FP8) asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(qf[qb][ks]));
+      else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(qf[qb][ks]));
+    }
+  };
+  // 24 wait states after the last score MFMA into s and before a VALU reads it (an 8-pass bf16
+  // result needs 11, a 16-pass e4m3 one 19)
+  auto score_drain = [&](f32x16 (&s)[2]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+  };
+
+  // ---- softmax pieces ------------------------------------------------------------------------
   f32x16 o[2][D / 32];  // in AGPRs (see mfma_acc_agpr)
   float m[2], l[2];     // reference max (exp2 units) and this lane's half of the row sum
-  float mr[2];          // running max of the scaled scores, for the overflow check
-  // LDS byte addresses of the two buffers, for the fills
-  const uint32_t ska0 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[0], ska1 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[1];
-  const uint32_t sva0 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[0], sva1 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[1];
-
-  // S^T = K.Q^T for both query blocks over one 64-key tile in LDS; keys past nvalid get -inf.
-  auto scores = [&](const uint8_t* sk, int nvalid, f32x16 (&s)[2][2]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[qb][kb][i] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krow = 32 * kb + sigma(l32);
-      if constexpr (FP8) {
-        i32x8 a[QREGS];
-#pragma unroll
-        for (int ks = 0; ks < QREGS; ++ks) {
-          const int g0 = 4 * ks + 2 * hi;
-          const i32x4 a0 = *reinterpret_cast<const i32x4*>(sk + Loader::kswz_off(krow, g0));
-          const i32x4 a1 = *reinterpret_cast<const i32x4*>(sk + Loader::kswz_off(krow, g0 + 1));
-          a[ks] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int ks = 0; ks < QREGS; ++ks) {
-          s[0][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks], qf[0][ks], s[0][kb], 0, 0, 0, 0, 0, 0);
-          s[1][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks], qf[1][ks], s[1][kb], 0, 0, 0, 0, 0, 0);
-        }
-      } else {
-        bf16x8 a[QREGS];
-#pragma unroll
-        for (int ks = 0; ks < QREGS; ++ks)
-          a[ks] = *reinterpret_cast<const bf16x8*>(sk + Loader::kswz_off(krow, 2 * ks + hi));
-#pragma unroll
-        for (int ks = 0; ks < QREGS; ++ks) {
-          s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[0][ks], s[0][kb], 0, 0, 0);
-          s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[1][ks], s[1][kb], 0, 0, 0);
-        }
-      }
-    }
-    if (nvalid < BN) {  // last tile of a chunk: keys past its end do not exist
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * kb + 16 * (i / 8) + 8 * hi + (i % 8) >= nvalid) s[qb][kb][i] = -INFINITY;
-    }
-  };
-  // max over this lane's 32 scores of one query block, times the score multiplier
-  auto lane_max = [&](const f32x16 (&sq)[2], float mult) {
-    float a0 = max3(sq[0][0], sq[0][1], sq[0][2]), a1 = max3(sq[0][3], sq[0][4], sq[0][5]);
-    float a2 = max3(sq[1][0], sq[1][1], sq[1][2]), a3 = max3(sq[1][3], sq[1][4], sq[1][5]);
-#pragma unroll
-    for (int i = 6; i < 16; i += 2) {
-      a0 = max3(a0, sq[0][i], sq[0][i + 1]);
-      a2 = max3(a2, sq[1][i], sq[1][i + 1]);
-    }
-    return max3(a1, a3, fmaxf(a0, a2)) * mult;
-  };
-
-  int cur_row0, cur_nv, nxt_row0, nxt_nv;  // tile descriptors, read one tile ahead
-
-  // One key tile: compute from buffer `buf` while the other buffer fills with the next tile.
-  // Order inside the tile (one wave, two query blocks):
-  //   scores of keys 0-31, then keys 32-63 (K operands shared by both blocks)
-  //   P of keys 0-31 (overlaps the second half of the score MFMAs)
-  //   P.V of keys 0-31, interleaved region by region with P of keys 32-63
-  //   P.V of keys 32-63
-  // The P.V MFMAs are inline asm (see mfma_acc_agpr), which the scheduler cannot interleave with
-  // VALU on its own, so the regions are fenced with sched_barrier.
-  auto tile = [&](int kt, int buf) {
-    const bool has_next = kt + 1 < kt1;
-    // the other buffer was last read before the previous barrier: refill it now, wait at the end
-    if (has_next) Loader::issue(kbase, p.v, nxt_row0, nxt_nv, head, H, buf ? ska0 : ska1, buf ? sva0 : sva1);
-    int n2_row0 = 0, n2_nv = 0;
-    if (kt + 2 < kt1) {
-      n2_row0 = ld_const(tiles, 2 * kt + 4);
-      n2_nv = ld_const(tiles, 2 * kt + 5);
-    }
-    float ksc = 1.f;
-    if constexpr (FP8) ksc = ld_const(p.k_scale, (cur_row0 / 64) * H + head);
-    if (wave_active) {
-      f32x16 s[2][2];  // [query block][32-key block]
-      float cm[2];
-      // P = exp2(s * cm - m) rounded to bf16, 8 keys (one MFMA k-step) at a time; the row sum is
-      // taken over the same rounded values (v_dot2 with ones), so the weights that multiply V
-      // sum exactly to the normaliser.
-      bf16x8 pb[2][4];
-      float rs[2] = {0.f, 0.f};
-      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-      auto make_p = [&](int qb, int k2) {
-        const int kb = k2 >> 1, b = 8 * (k2 & 1);
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[qb][kb][b + j], cm[qb], -m[qb]));
-        pb[qb][k2] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-        float r = rs[qb];
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 0, 1), ones, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 2, 3), ones, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 4, 5), ones, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 6, 7), ones, r, false);
-        rs[qb] = r;
-      };
-      // front half (does not touch O): scores, running max, P of keys 0-31; specialised for the
-      // ragged last tile of a chunk so that the common tile has no masking branch inside
-      auto front = [&](auto ragged) {
-        scores(smem_k[buf], decltype(ragged)::value ? cur_nv : BN, s);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          cm[qb] = cq[qb] * ksc;  // > 0, so scaling commutes with the max
-          mr[qb] = fmaxf(mr[qb], lane_max(s[qb], cm[qb]));
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          make_p(qb, 0);
-          make_p(qb, 1);
-        }
-      };
-      if (cur_nv < BN) front(std::integral_constant<bool, true>());
-      else front(std::integral_constant<bool, false>());
-      const uint16_t* sv = smem_v[buf];
-      const int t = lane & 15, G = lane >> 4;
-      // V^T operand of (d block cb, key step k2) through two transposed LDS reads
-      auto v_op = [&](int cb, int k2) {
-        const int row = 16 * k2 + 8 * hi + (t >> 2);
-        const int col = 32 * cb + 16 * (G & 1) + 4 * (t & 3);
-        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WF_LDS i16x4*)(sv + lds_off<D>(row, col)));
-        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WF_LDS i16x4*)(sv + lds_off<D>(row + 4, col)));
-        // whole-vector concatenation: element-wise 16-bit inserts are lowered wrongly by this
-        // compiler (they reuse the first dword of each transposed read)
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8 va[D / 32][2];
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        va[cb][0] = v_op(cb, 0);
-        va[cb][1] = v_op(cb, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // P.V of keys 0-31 (k2 = 0, 1), each pair of MFMAs followed by a quarter of one query
-      // block's P for keys 32-63
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          mfma_acc_agpr(o[0][cb], va[cb][k2], pb[0][k2]);
-          mfma_acc_agpr(o[1][cb], va[cb][k2], pb[1][k2]);
-          const int u = 2 * cb + k2;  // 0..7 for d = 128: (qb, k2') = (u / 4, 2 + (u / 2) % 2)
-          if constexpr (D == 128) {
-            if ((u & 1) == 0) make_p(u >> 2, 2 + ((u >> 1) & 1));
-          } else {
-            make_p(u >> 1, 2 + (u & 1));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // P.V of keys 32-63
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const bf16x8 a2 = v_op(cb, 2), a3 = v_op(cb, 3);
-        mfma_acc_agpr(o[0][cb], a2, pb[0][2]);
-        mfma_acc_agpr(o[1][cb], a2, pb[1][2]);
-        mfma_acc_agpr(o[0][cb], a3, pb[0][3]);
-        mfma_acc_agpr(o[1][cb], a3, pb[1][3]);
-      }
-      l[0] += rs[0];
-      l[1] += rs[1];
-    }
-    lds_fill_barrier();
-    cur_row0 = nxt_row0;
-    cur_nv = nxt_nv;
-    nxt_row0 = n2_row0;
-    nxt_nv = n2_nv;
-  };
-
-  // Pass 0 takes its reference from the first tile; pass 1 (rare) uses the true max of pass 0.
-  for (int pass = 0; pass < 2; ++pass) {
+  auto clear_o = [&]() {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -338,38 +297,260 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       }
       l[qb] = 0.f;
     }
-    cur_row0 = ld_const(tiles, 2 * kt0);
-    cur_nv = ld_const(tiles, 2 * kt0 + 1);
-    nxt_row0 = 0;
-    nxt_nv = 0;
-    if (kt0 + 1 < kt1) {
-      nxt_row0 = ld_const(tiles, 2 * kt0 + 2);
-      nxt_nv = ld_const(tiles, 2 * kt0 + 3);
-    }
-    Loader::issue(kbase, p.v, cur_row0, cur_nv, head, H, ska0, sva0);
-    lds_fill_barrier();
-    if (pass == 0 && wave_active) {
-      // the reference: the max of the first tile (its scores are recomputed by the loop)
-      float ksc = 1.f;
-      if constexpr (FP8) ksc = ld_const(p.k_scale, (cur_row0 / 64) * H + head);
-      f32x16 s[2][2];
-      scores(smem_k[0], cur_nv, s);
+  };
+  // keys of half kb at or past nvalid do not exist: their scores become -inf
+  auto mask_half = [&](f32x16 (&s)[2], int kb, int nvalid) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        m[qb] = pair_max(lane_max(s[qb], cq[qb] * ksc));
-        mr[qb] = m[qb];
-      }
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * kb + 16 * (i / 8) + 8 * hi + (i % 8) >= nvalid) s[qb][i] = -INFINITY;
+  };
+  // full score tile (both halves), used outside the pipelined loop
+  auto scores_tile = [&](const uint8_t* sk, int nvalid, f32x16 (&s0)[2], f32x16 (&s1)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16(&s)[2] = kb ? s1 : s0;
+      static_for<0, QREGS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        const KVec a = k_op(sk, kb, ks);
+        s_mfma(s[0], a, 0, ks, std::integral_constant<bool, ks == 0>());
+        s_mfma(s[1], a, 1, ks, std::integral_constant<bool, ks == 0>());
+      });
     }
-    for (int kt = kt0; kt < kt1; ++kt) tile(kt, (kt - kt0) & 1);
-    // Did any score exceed the reference by more than 2^64?  Decided for the whole workgroup, so
-    // that every wave runs the same number of tiles (and barriers).
+    score_drain(s0);
+    score_drain(s1);
+    if (nvalid < BN) {
+      mask_half(s0, 0, nvalid);
+      mask_half(s1, 1, nvalid);
+    }
+  };
+  // max over this lane's 32 scores of one query block (two halves), times the score multiplier
+  auto lane_max = [&](const f32x16& a, const f32x16& b, float mult) {
+    float a0 = max3(a[0], a[1], a[2]), a1 = max3(a[3], a[4], a[5]);
+    float a2 = max3(b[0], b[1], b[2]), a3 = max3(b[3], b[4], b[5]);
+#pragma unroll
+    for (int i = 6; i < 16; i += 2) {
+      a0 = max3(a0, a[i], a[i + 1]);
+      a2 = max3(a2, b[i], b[i + 1]);
+    }
+    return max3(a1, a3, fmaxf(a0, a2)) * mult;
+  };
+
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  // state of the VALU program for one half: exponent temporaries, packed pairs
+  struct ValuState {
+    float t[32];
+    uint32_t pw[16];
+  };
+  auto valu_op = [&](auto kc, ValuState& st, const f32x16 (&s)[2], const float (&cm)[2]) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int kind = kValu.kind[k], e = kValu.idx[k];
+    if constexpr (kind == OP_F) {
+      st.t[e] = fmaf(s[e >> 4][e & 15], cm[e >> 4], -m[e >> 4]);
+    } else if constexpr (kind == OP_X) {
+      st.t[e] = fast_exp2(st.t[e]);
+    } else if constexpr (kind == OP_C) {
+      st.pw[e] = pack2_bf16(st.t[2 * e], st.t[2 * e + 1]);
+    } else {
+      l[e >> 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, st.pw[e]), ones, l[e >> 3], false);
+    }
+  };
+  auto anchor_l = [&]() { asm volatile("" ::"v"(l[0]), "v"(l[1])); };
+  auto p_operands = [&](const ValuState& st, bf16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int b = 8 * qb + 4 * k2;
+        const i32x4 w = {(int)st.pw[b], (int)st.pw[b + 1], (int)st.pw[b + 2], (int)st.pw[b + 3]};
+        pb[qb][k2] = __builtin_bit_cast(bf16x8, w);
+      }
+  };
+  // P for one half without interleaving (prologue)
+  auto make_p_plain = [&](const f32x16 (&s)[2], const float (&cm)[2], bf16x8 (&pb)[2][2]) {
+    ValuState st;
+    static_for<0, 96>([&](auto kc) { valu_op(kc, st, s, cm); });
+    p_operands(st, pb);
+  };
+
+  // One half step.  MFMAs: (if HAS_S) the scores of half kb_next from K buffer sk into s_next, and
+  // the P.V of half `half` of the tile in V buffer sv with pb_in.  Between them, (if HAS_P) the VALU
+  // program turning s_src into pb_out.
+  constexpr int NS_FULL = 2 * QREGS;  // score MFMAs per half
+  constexpr int NP = D / 8;           // P.V MFMAs per half: 2 blocks x D/32 x 2 k-steps
+  constexpr int LA = 3;               // operand loads run this many MFMA regions ahead
+  auto half_step = [&](auto has_s, auto has_p, const uint8_t* sk, int kb_next, f32x16 (&s_next)[2],
+                       const uint16_t* sv, int half, const bf16x8 (&pb_in)[2][2],
+                       const f32x16 (&s_src)[2], const float (&cm)[2], bf16x8 (&pb_out)[2][2]) {
+    constexpr bool HS = decltype(has_s)::value, HP = decltype(has_p)::value;
+    constexpr int NS = HS ? NS_FULL : 0;
+    constexpr int NR = NS + NP;
+    constexpr int NKOP = HS ? QREGS : 0;  // K operands (each feeds both query blocks)
+    constexpr int NVOP = NP / 2;          // V operands (each feeds both query blocks)
+    KVec kop[QREGS];
+    bf16x8 vop[NVOP];
+    auto load_for = [&](auto rc) {  // operands whose first use is region r
+      constexpr int r = decltype(rc)::value;
+      static_for<0, NKOP>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (k_first_use(ks, NS, NP) == r) kop[ks] = k_op(sk, kb_next, ks);
+      });
+      static_for<0, NVOP>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (v_first_use(t, NS, NP) == r) vop[t] = v_op(sv, t >> 1, 2 * half + (t & 1));
+      });
+    };
+    ValuState st;
+    static_for<0, LA>(load_for);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NR>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      constexpr int idx = region_index(r, NS, NP);
+      if constexpr (region_is_s(r, NS, NP)) {
+        constexpr int qb = idx & 1, ks = idx >> 1;
+        s_mfma(s_next[qb], kop[ks], qb, ks, std::integral_constant<bool, ks == 0>());
+      } else {
+        constexpr int qb = idx & 1, t = idx >> 1;
+        mfma_acc_agpr(o[qb][t >> 1], vop[t], pb_in[qb][t & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HP) static_for<(r * 96) / NR, ((r + 1) * 96) / NR>([&](auto kc) { valu_op(kc, st, s_src, cm); });
+      if constexpr (r + LA < NR) load_for(std::integral_constant<int, r + LA>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (HP) {
+      p_operands(st, pb_out);
+      // Keep this step's VALU results in this step: without a use here the compiler may sink
+      // them past a following branch into the next step, away from the MFMAs they overlap.
+      asm volatile("" ::"v"(pb_out[0][0]), "v"(pb_out[0][1]), "v"(pb_out[1][0]), "v"(pb_out[1][1]));
+      anchor_l();
+    }
+  };
+
+  // ---- the key loop ------------------------------------------------------------------------
+  // Ring: slot s (s >= -1) holds K of tile s+1 and V of tile s, in buffer (s+1) % 3.  Iteration j
+  // reads slot j (scores of tile j+1, P.V of tile j) and fills slot j+2.
+  auto fill_slot = [&](auto bufc, int s) {  // s: slot; tiles are relative to kt0
+    constexpr int B = decltype(bufc)::value;
+    const uint32_t ka = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[B];
+    const uint32_t va = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[B];
+    if (s + 1 < n) ld.fill_k(kpool, ld_const(tiles, 2 * (kt0 + s + 1)), ld_const(tiles, 2 * (kt0 + s + 1) + 1), head, H, ka);
+    if (s >= 0 && s < n) ld.fill_v(vpool, ld_const(tiles, 2 * (kt0 + s)), ld_const(tiles, 2 * (kt0 + s) + 1), head, H, va);
+  };
+  // wait until only the loads of slot s (issued last) may still be in flight
+  auto wait_all_but_slot = [&](int s) {
+    const bool kpart = s + 1 < n, vpart = s >= 0 && s < n;
+    if (kpart && vpart) wait_vmcnt<KI + VI>();
+    else if (vpart) wait_vmcnt<VI>();
+    else if (kpart) wait_vmcnt<KI>();
+    else wait_vmcnt<0>();
+  };
+  auto tile_nv = [&](int j) { return ld_const(tiles, 2 * (kt0 + j) + 1); };
+  auto tile_cm = [&](int j, float (&cm)[2]) {
+    float ksc = 1.f;
+    if constexpr (FP8) ksc = ld_const(p.k_scale, (ld_const(tiles, 2 * (kt0 + j)) / 64) * H + head);
+    cm[0] = cq[0] * ksc;  // > 0, so scaling commutes with the max
+    cm[1] = cq[1] * ksc;
+  };
+
+  bool fixed_m = false;  // pass 1: m already holds the true row max
+  for (int pass = 0; pass < 2; ++pass) {
+    clear_o();
+    // prologue: slots -1, 0, 1 in flight; wait for slot -1 (K of tile 0)
+    fill_slot(std::integral_constant<int, 0>(), -1);
+    fill_slot(std::integral_constant<int, 1>(), 0);
+    if (n > 1) fill_slot(std::integral_constant<int, 2>(), 1);
+    {
+      const bool k1 = n > 1, k2 = n > 2;  // loads issued after slot -1
+      if (k2) wait_vmcnt<2 * KI + 2 * VI>();
+      else if (k1) wait_vmcnt<KI + 2 * VI>();
+      else wait_vmcnt<VI>();
+    }
+    __syncthreads();
+    f32x16 s_a[2];      // scores of the current tile's second half
+    bf16x8 p_a[2][2];   // P of the current tile's first half
+    float cm_cur[2];
+    tile_cm(0, cm_cur);
+    int nv_cur = tile_nv(0);
+    if (wave_active) {
+      f32x16 s0[2];
+      scores_tile(reinterpret_cast<const uint8_t*>(smem_k[0]), nv_cur, s0, s_a);
+      if (!fixed_m) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) m[qb] = pair_max(lane_max(s0[qb], s_a[qb], cm_cur[qb]));
+      }
+      make_p_plain(s0, cm_cur, p_a);
+    }
+    wait_all_but_slot(1);
+    __syncthreads();
+
+    // iteration j reads slot j (buffer B, a compile-time constant so that every LDS address is a
+    // per-lane base plus an immediate offset) and refills buffer (B + 2) % 3 with slot j+2
+    auto step = [&](auto bufc, int j) {
+      constexpr int B = decltype(bufc)::value;
+      fill_slot(std::integral_constant<int, (B + 2) % NBUF>(), j + 2);
+      const int nv_nxt = tile_nv(j + 1);
+      float cm_nxt[2];
+      tile_cm(j + 1, cm_nxt);
+      if (wave_active) {
+        const uint8_t* sk = reinterpret_cast<const uint8_t*>(smem_k[B]);
+        const uint16_t* sv = smem_v[B];
+        if (nv_cur < BN) {  // tile j is a chunk's last, partial tile
+          score_drain(s_a);
+          mask_half(s_a, 1, nv_cur);
+        }
+        // A: scores of tile j+1 half 0; P.V of tile j half 0; P of tile j half 1
+        f32x16 s_n0[2];
+        bf16x8 p_1[2][2];
+        half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, p_1);
+        if (nv_nxt < BN) {
+          score_drain(s_n0);
+          mask_half(s_n0, 0, nv_nxt);
+        }
+        // B: scores of tile j+1 half 1; P.V of tile j half 1; P of tile j+1 half 0
+        half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, p_a);
+      }
+      cm_cur[0] = cm_nxt[0];
+      cm_cur[1] = cm_nxt[1];
+      nv_cur = nv_nxt;
+      wait_all_but_slot(j + 2);
+      __syncthreads();
+    };
+    // last tile (slot n-1, buffer B): P.V only
+    // last tile (slot n-1, buffer n % 3): P.V only.  One instantiation with a runtime buffer, so
+    // that O flows through a single path (a branch per buffer would make the register allocator
+    // copy O between AGPRs, and such copies cannot be ordered after the asm MFMAs that write O).
+    auto last = [&](int b) {
+      if (wave_active) {
+        const uint16_t* sv = smem_v[b];
+        if (nv_cur < BN) {
+          score_drain(s_a);
+          mask_half(s_a, 1, nv_cur);
+        }
+        f32x16 dummy[2];
+        bf16x8 p_1[2][2], p_unused[2][2];
+        half_step(std::false_type(), std::true_type(), nullptr, 0, dummy, sv, 0, p_a, s_a, cm_cur, p_1);
+        half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, p_unused);
+      }
+    };
+    for (int j = 0;;) {
+      if (j + 1 >= n) break;
+      step(std::integral_constant<int, 1>(), j++);
+      if (j + 1 >= n) break;
+      step(std::integral_constant<int, 2>(), j++);
+      if (j + 1 >= n) break;
+      step(std::integral_constant<int, 0>(), j++);
+    }
+    last(n % NBUF);
+    __syncthreads();  // the ring is refilled by the next pass or segment
+
+    // Could some P have overflowed?  Decided for the whole workgroup, so that every wave runs the
+    // same number of tiles (and barriers).
     bool redo = false;
-    if (wave_active && pass == 0) {
+    if (wave_active && !fixed_m) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        mr[qb] = pair_max(mr[qb]);
-        redo = redo || (mr[qb] > m[qb] + 64.f);
-      }
+      for (int qb = 0; qb < 2; ++qb) redo = redo || !(pair_sum(l[qb]) < 0x1p64f);
     }
     const bool wave_redo = __any(redo);
     if (lane == 0) redo_flags[wave] = wave_redo ? 1 : 0;
@@ -377,8 +558,25 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     const bool any_redo = (redo_flags[0] | redo_flags[1] | redo_flags[2] | redo_flags[3]) != 0;
     __syncthreads();  // flags are rewritten by the next segment
     if (!any_redo) break;
+    // score-only sweep for the true row max (rare path, one buffer, no overlap)
+    float mr[2] = {-INFINITY, -INFINITY};
+    for (int j = 0; j < n; ++j) {
+      ld.fill_k(kpool, ld_const(tiles, 2 * (kt0 + j)), tile_nv(j), head, H, (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[0]);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (wave_active) {
+        float cm[2];
+        tile_cm(j, cm);
+        f32x16 s0[2], s1[2];
+        scores_tile(reinterpret_cast<const uint8_t*>(smem_k[0]), tile_nv(j), s0, s1);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) m[qb] = mr[qb];
+        for (int qb = 0; qb < 2; ++qb) mr[qb] = fmaxf(mr[qb], lane_max(s0[qb], s1[qb], cm[qb]));
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) m[qb] = pair_max(mr[qb]);
+    fixed_m = true;
   }
 
   if (!wave_active) return;
@@ -428,8 +626,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
 template <int D, bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
   using Loader = TileLoader<D, FP8>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_k[2][BN * Loader::KB];
-  __shared__ __attribute__((aligned(16))) uint16_t smem_v[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint8_t smem_k[NBUF][BN * Loader::KB];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_v[NBUF][BN * D];
   __shared__ int redo_flags[NTHR / 64];
   const int32_t* hdr = p.blob;
   if (ld_const(hdr, H_NONCE_LO) != (int32_t)p.nonce_lo || ld_const(hdr, H_NONCE_HI) != (int32_t)p.nonce_hi) return;
