@@ -70,6 +70,7 @@ struct TileLoader {
   static constexpr int VI = BN * D * 2 / 1024 / 4;
 
   uint32_t koff[KI], voff[VI];
+  int wave_u;  // wave index, uniform
 
   // Byte offset of granule g of K row r.  bf16: the same swizzle as V.  e4m3: rows are D bytes,
   // so 256/D rows share one 64-bank line; XOR with (r / (256/D)) spreads 16 rows of one granule
@@ -95,6 +96,7 @@ struct TileLoader {
 
   __device__ __forceinline__ void init(int head, int H) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int j = 0; j < KI; ++j) koff[j] = k_src(wave, j, lane, BN, head, H);
 #pragma unroll
@@ -111,7 +113,7 @@ struct TileLoader {
   // K of the tile whose first key is pool row row0, into the LDS buffer at byte address lds.
   __device__ __forceinline__ void fill_k(const uint8_t* kpool, int row0, int nvalid, int head, int H, uint32_t lds) const {
     const uint8_t* base = kpool + (size_t)row0 * H * KB;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wave_u;
     if (nvalid == BN) {
 #pragma unroll
       for (int j = 0; j < KI; ++j) dma16(lds + (wave * KI + j) * 1024, koff[j], base);
@@ -123,7 +125,7 @@ struct TileLoader {
   }
   __device__ __forceinline__ void fill_v(const uint8_t* vpool, int row0, int nvalid, int head, int H, uint32_t lds) const {
     const uint8_t* base = vpool + (size_t)row0 * H * 2 * D;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wave_u;
     if (nvalid == BN) {
 #pragma unroll
       for (int j = 0; j < VI; ++j) dma16(lds + (wave * VI + j) * 1024, voff[j], base);
@@ -201,6 +203,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const bool wave_active = 64 * wave < q_rows;
   const int n = kt1 - kt0;
+  const int rot_of_segment = p.rot_delta > 0 ? ((q_row0 / BM) * p.rot_delta) % n : 0;
 
   Loader ld;
   ld.init(head, H);
@@ -431,12 +434,35 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   // ---- the key loop ------------------------------------------------------------------------
   // Ring: slot s (s >= -1) holds K of tile s+1 and V of tile s, in buffer (s+1) % 3.  Iteration j
   // reads slot j (scores of tile j+1, P.V of tile j) and fills slot j+2.
-  auto fill_slot = [&](auto bufc, int s) {  // s: slot; tiles are relative to kt0
+  // The segment's tiles are visited from position `rot` on, wrapping around (softmax does not
+  // depend on the key order).  Staggering the start of the query tiles of one head lets the
+  // later ones find each K/V tile already in the XCD's L2.
+  const int rot = rot_of_segment;
+  auto tix = [&](int j) {  // absolute index of the j-th visited tile
+    const int r = j + rot;
+    return 2 * (kt0 + (r < n ? r : r - n));
+  };
+  // Tile descriptors (first pool row, valid keys) are read with scalar loads one step before
+  // they are needed, so no step waits on a scalar load.
+  struct Desc {
+    int row0, nv;
+  };
+  auto load_desc = [&](int j) -> Desc {
+    if (j >= n) return Desc{0, BN};  // past the segment: never used for a fill
+    const int t = tix(j);
+    return Desc{ld_const(tiles, t), ld_const(tiles, t + 1)};
+  };
+  auto k_scale_of = [&](const Desc& d) -> float {
+    if constexpr (FP8) return ld_const(p.k_scale, (d.row0 / 64) * H + head);
+    else return 1.f;
+  };
+  // slot s: K of tile s+1 (descriptor dk) and V of tile s (descriptor dv), into buffer B
+  auto fill_slot = [&](auto bufc, int s, const Desc& dk, const Desc& dv) {
     constexpr int B = decltype(bufc)::value;
     const uint32_t ka = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[B];
     const uint32_t va = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[B];
-    if (s + 1 < n) ld.fill_k(kpool, ld_const(tiles, 2 * (kt0 + s + 1)), ld_const(tiles, 2 * (kt0 + s + 1) + 1), head, H, ka);
-    if (s >= 0 && s < n) ld.fill_v(vpool, ld_const(tiles, 2 * (kt0 + s)), ld_const(tiles, 2 * (kt0 + s) + 1), head, H, va);
+    if (s + 1 < n) ld.fill_k(kpool, dk.row0, dk.nv, head, H, ka);
+    if (s >= 0 && s < n) ld.fill_v(vpool, dv.row0, dv.nv, head, H, va);
   };
   // wait until only the loads of slot s (issued last) may still be in flight
   auto wait_all_but_slot = [&](int s) {
@@ -446,10 +472,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     else if (kpart) wait_vmcnt<KI>();
     else wait_vmcnt<0>();
   };
-  auto tile_nv = [&](int j) { return ld_const(tiles, 2 * (kt0 + j) + 1); };
-  auto tile_cm = [&](int j, float (&cm)[2]) {
-    float ksc = 1.f;
-    if constexpr (FP8) ksc = ld_const(p.k_scale, (ld_const(tiles, 2 * (kt0 + j)) / 64) * H + head);
+  auto set_cm = [&](float ksc, float (&cm)[2]) {
     cm[0] = cq[0] * ksc;  // > 0, so scaling commutes with the max
     cm[1] = cq[1] * ksc;
   };
@@ -458,9 +481,11 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   for (int pass = 0; pass < 2; ++pass) {
     clear_o();
     // prologue: slots -1, 0, 1 in flight; wait for slot -1 (K of tile 0)
-    fill_slot(std::integral_constant<int, 0>(), -1);
-    fill_slot(std::integral_constant<int, 1>(), 0);
-    if (n > 1) fill_slot(std::integral_constant<int, 2>(), 1);
+    const Desc d0 = load_desc(0);
+    Desc d1 = load_desc(1), d2 = load_desc(2), d3 = load_desc(3);  // tiles j+1, j+2, j+3 of step j
+    fill_slot(std::integral_constant<int, 0>(), -1, d0, d0);
+    fill_slot(std::integral_constant<int, 1>(), 0, d1, d0);
+    if (n > 1) fill_slot(std::integral_constant<int, 2>(), 1, d2, d1);
     {
       const bool k1 = n > 1, k2 = n > 2;  // loads issued after slot -1
       if (k2) wait_vmcnt<2 * KI + 2 * VI>();
@@ -471,8 +496,9 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     f32x16 s_a[2];      // scores of the current tile's second half
     bf16x8 p_a[2][2];   // P of the current tile's first half
     float cm_cur[2];
-    tile_cm(0, cm_cur);
-    int nv_cur = tile_nv(0);
+    set_cm(k_scale_of(d0), cm_cur);
+    float ksc_nxt = k_scale_of(d1);
+    int nv_cur = d0.nv;
     if (wave_active) {
       f32x16 s0[2];
       scores_tile(reinterpret_cast<const uint8_t*>(smem_k[0]), nv_cur, s0, s_a);
@@ -489,10 +515,18 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     // per-lane base plus an immediate offset) and refills buffer (B + 2) % 3 with slot j+2
     auto step = [&](auto bufc, int j) {
       constexpr int B = decltype(bufc)::value;
-      fill_slot(std::integral_constant<int, (B + 2) % NBUF>(), j + 2);
-      const int nv_nxt = tile_nv(j + 1);
+      // d3 was loaded during the previous step; using it only from here on keeps the compiler
+      // from deriving values from it (and waiting for the load) right after the load
+      d3.row0 = __builtin_amdgcn_readfirstlane(d3.row0);
+      d3.nv = __builtin_amdgcn_readfirstlane(d3.nv);
+      asm volatile("" : "+s"(d3.row0), "+s"(d3.nv));
+      fill_slot(std::integral_constant<int, (B + 2) % NBUF>(), j + 2, d3, d2);
+      // descriptors for the next step
+      const Desc d4 = load_desc(j + 4);
+      const float ksc_n2 = k_scale_of(d2);
+      const int nv_nxt = d1.nv;
       float cm_nxt[2];
-      tile_cm(j + 1, cm_nxt);
+      set_cm(ksc_nxt, cm_nxt);
       if (wave_active) {
         const uint8_t* sk = reinterpret_cast<const uint8_t*>(smem_k[B]);
         const uint16_t* sv = smem_v[B];
@@ -514,10 +548,13 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       cm_cur[0] = cm_nxt[0];
       cm_cur[1] = cm_nxt[1];
       nv_cur = nv_nxt;
+      d1 = d2;
+      d2 = d3;
+      d3 = d4;
+      ksc_nxt = ksc_n2;
       wait_all_but_slot(j + 2);
       __syncthreads();
     };
-    // last tile (slot n-1, buffer B): P.V only
     // last tile (slot n-1, buffer n % 3): P.V only.  One instantiation with a runtime buffer, so
     // that O flows through a single path (a branch per buffer would make the register allocator
     // copy O between AGPRs, and such copies cannot be ordered after the asm MFMAs that write O).
@@ -561,14 +598,15 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     // score-only sweep for the true row max (rare path, one buffer, no overlap)
     float mr[2] = {-INFINITY, -INFINITY};
     for (int j = 0; j < n; ++j) {
-      ld.fill_k(kpool, ld_const(tiles, 2 * (kt0 + j)), tile_nv(j), head, H, (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[0]);
+      const Desc dj = load_desc(j);
+      ld.fill_k(kpool, dj.row0, dj.nv, head, H, (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[0]);
       wait_vmcnt<0>();
       __syncthreads();
       if (wave_active) {
         float cm[2];
-        tile_cm(j, cm);
+        set_cm(k_scale_of(dj), cm);
         f32x16 s0[2], s1[2];
-        scores_tile(reinterpret_cast<const uint8_t*>(smem_k[0]), tile_nv(j), s0, s1);
+        scores_tile(reinterpret_cast<const uint8_t*>(smem_k[0]), dj.nv, s0, s1);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) mr[qb] = fmaxf(mr[qb], lane_max(s0[qb], s1[qb], cm[qb]));
       }
