@@ -103,6 +103,26 @@ struct TileLoader {
     for (int j = 0; j < VI; ++j) voff[j] = v_src(wave, j, lane, BN, head, H);
   }
 
+  // Per-lane source offsets of this wave's loads for a tile with nvalid valid keys.
+  __device__ __forceinline__ void k_offsets(int nvalid, int head, int H, uint32_t (&o)[KI]) const {
+    if (nvalid == BN) {
+#pragma unroll
+      for (int j = 0; j < KI; ++j) o[j] = koff[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KI; ++j) o[j] = k_src(wave_u, j, threadIdx.x & 63, nvalid, head, H);
+    }
+  }
+  __device__ __forceinline__ void v_offsets(int nvalid, int head, int H, uint32_t (&o)[VI]) const {
+    if (nvalid == BN) {
+#pragma unroll
+      for (int j = 0; j < VI; ++j) o[j] = voff[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < VI; ++j) o[j] = v_src(wave_u, j, threadIdx.x & 63, nvalid, head, H);
+    }
+  }
+
   // The fills are inline asm so that the compiler does not treat them as LDS stores: it would
   // otherwise wait for every in-flight fill before each LDS read.  Completion is awaited with
   // explicit vmcnt waits.  M0 carries the LDS destination of global_load_lds; nothing else in
@@ -138,20 +158,24 @@ struct TileLoader {
 };
 
 // The VALU work that turns 32 scores per lane (2 query blocks x 16 keys) into bf16 P and the row
-// sums, as 96 operations in a software-pipelined order: for element e, F(e) = fma(s, c, -m),
-// X(e) = exp2, then per pair of elements C = convert to bf16x2 and D = add to the row sum.  Each
-// operation depends only on operations at least two places earlier in the list, so any run of
-// consecutive operations can be issued between two MFMAs without waiting on each other.
-enum : int { OP_F = 0, OP_X = 1, OP_C = 2, OP_D = 3 };
+// sums, as 112 operations in a software-pipelined order: for element e, F(e) = fma(s, c, -m),
+// X(e) = exp2, per pair of elements C = convert to bf16x2, and A(e) = add the bf16-rounded weight
+// (unpacked from its pair) to the row sum, so that the weights that multiply V sum exactly to the
+// normaliser.  Each operation depends only on operations at least two places earlier in the
+// list, so any run of consecutive operations can be issued between two MFMAs without waiting on
+// each other.  (The row sum uses v_add_f32 rather than v_dot2 on the bf16 pairs: v_dot2
+// instructions do not issue while an MFMA is executing.)
+enum : int { OP_F = 0, OP_X = 1, OP_C = 2, OP_A = 3 };
+constexpr int kValuOps = 112;
 struct ValuProgram {
-  int kind[96], idx[96];
+  int kind[kValuOps], idx[kValuOps];
   constexpr ValuProgram() : kind(), idx() {
     int n = 0;
     for (int s = 0; s < 36; ++s) {
       if (s < 32) { kind[n] = OP_F; idx[n] = s; ++n; }
       if (s >= 1 && s <= 32) { kind[n] = OP_X; idx[n] = s - 1; ++n; }
       if (s >= 3 && (s & 1) && (s - 3) / 2 < 16) { kind[n] = OP_C; idx[n] = (s - 3) / 2; ++n; }
-      if (s >= 4 && !(s & 1) && (s - 4) / 2 < 16) { kind[n] = OP_D; idx[n] = (s - 4) / 2; ++n; }
+      if (s >= 4) { kind[n] = OP_A; idx[n] = s - 4; ++n; }
     }
   }
 };
@@ -340,7 +364,6 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     return max3(a1, a3, fmaxf(a0, a2)) * mult;
   };
 
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   // state of the VALU program for one half: exponent temporaries, packed pairs
   struct ValuState {
     float t[32];
@@ -356,7 +379,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     } else if constexpr (kind == OP_C) {
       st.pw[e] = pack2_bf16(st.t[2 * e], st.t[2 * e + 1]);
     } else {
-      l[e >> 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, st.pw[e]), ones, l[e >> 3], false);
+      const uint32_t w = st.pw[e >> 1];
+      l[e >> 4] += __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     }
   };
   auto anchor_l = [&]() { asm volatile("" ::"v"(l[0]), "v"(l[1])); };
@@ -373,7 +397,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   // P for one half without interleaving (prologue)
   auto make_p_plain = [&](const f32x16 (&s)[2], const float (&cm)[2], bf16x8 (&pb)[2][2]) {
     ValuState st;
-    static_for<0, 96>([&](auto kc) { valu_op(kc, st, s, cm); });
+    static_for<0, kValuOps>([&](auto kc) { valu_op(kc, st, s, cm); });
     p_operands(st, pb);
   };
 
@@ -383,10 +407,16 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   constexpr int NS_FULL = 2 * QREGS;  // score MFMAs per half
   constexpr int NP = D / 8;           // P.V MFMAs per half: 2 blocks x D/32 x 2 k-steps
   constexpr int LA = 3;               // operand loads run this many MFMA regions ahead
+  //
+  // It also issues ND tile fills (global -> LDS, 1 KB per wave each, offsets doff, LDS byte
+  // address dlds + 1024 j, global base dbase), spread evenly over its MFMA regions so that the
+  // memory pipeline takes them in the background instead of stalling the wave on a burst.
   auto half_step = [&](auto has_s, auto has_p, const uint8_t* sk, int kb_next, f32x16 (&s_next)[2],
                        const uint16_t* sv, int half, const bf16x8 (&pb_in)[2][2],
-                       const f32x16 (&s_src)[2], const float (&cm)[2], bf16x8 (&pb_out)[2][2]) {
+                       const f32x16 (&s_src)[2], const float (&cm)[2], bf16x8 (&pb_out)[2][2],
+                       auto ndc, const uint32_t* doff, uint32_t dlds, const uint8_t* dbase) {
     constexpr bool HS = decltype(has_s)::value, HP = decltype(has_p)::value;
+    constexpr int ND = decltype(ndc)::value;
     constexpr int NS = HS ? NS_FULL : 0;
     constexpr int NR = NS + NP;
     constexpr int NKOP = HS ? QREGS : 0;  // K operands (each feeds both query blocks)
@@ -418,7 +448,11 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         mfma_acc_agpr(o[qb][t >> 1], vop[t], pb_in[qb][t & 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (HP) static_for<(r * 96) / NR, ((r + 1) * 96) / NR>([&](auto kc) { valu_op(kc, st, s_src, cm); });
+      static_for<0, ND>([&](auto dc) {
+        constexpr int dj = decltype(dc)::value;
+        if constexpr (((2 * dj + 1) * NR) / (2 * ND) == r) Loader::dma16(dlds + 1024 * dj, doff[dj], dbase);
+      });
+      if constexpr (HP) static_for<(r * kValuOps) / NR, ((r + 1) * kValuOps) / NR>([&](auto kc) { valu_op(kc, st, s_src, cm); });
       if constexpr (r + LA < NR) load_for(std::integral_constant<int, r + LA>());
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -520,7 +554,17 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       d3.row0 = __builtin_amdgcn_readfirstlane(d3.row0);
       d3.nv = __builtin_amdgcn_readfirstlane(d3.nv);
       asm volatile("" : "+s"(d3.row0), "+s"(d3.nv));
-      fill_slot(std::integral_constant<int, (B + 2) % NBUF>(), j + 2, d3, d2);
+      // slot j+2 (K of tile j+3, V of tile j+2) is filled from inside the two half steps; past
+      // the segment's end the descriptors point at pool row 0, so every step issues the same
+      // number of (in-bounds) loads and the wait below is a constant
+      constexpr int FB = (B + 2) % NBUF;
+      uint32_t fko[KI], fvo[VI];
+      ld.k_offsets(d3.nv, head, H, fko);
+      ld.v_offsets(d2.nv, head, H, fvo);
+      const uint8_t* fkb = kpool + (size_t)d3.row0 * H * Loader::KB;
+      const uint8_t* fvb = vpool + (size_t)d2.row0 * H * 2 * D;
+      const uint32_t fkl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[FB] + ld.wave_u * KI * 1024;
+      const uint32_t fvl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[FB] + ld.wave_u * VI * 1024;
       // descriptors for the next step
       const Desc d4 = load_desc(j + 4);
       const float ksc_n2 = k_scale_of(d2);
@@ -537,13 +581,20 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         // A: scores of tile j+1 half 0; P.V of tile j half 0; P of tile j half 1
         f32x16 s_n0[2];
         bf16x8 p_1[2][2];
-        half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, p_1);
+        half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, p_1,
+                  std::integral_constant<int, KI>(), fko, fkl, fkb);
         if (nv_nxt < BN) {
           score_drain(s_n0);
           mask_half(s_n0, 0, nv_nxt);
         }
         // B: scores of tile j+1 half 1; P.V of tile j half 1; P of tile j+1 half 0
-        half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, p_a);
+        half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, p_a,
+                  std::integral_constant<int, VI>(), fvo, fvl, fvb);
+      } else {  // a wave without query rows still does its share of the fills
+#pragma unroll
+        for (int i = 0; i < KI; ++i) Loader::dma16(fkl + 1024 * i, fko[i], fkb);
+#pragma unroll
+        for (int i = 0; i < VI; ++i) Loader::dma16(fvl + 1024 * i, fvo[i], fvb);
       }
       cm_cur[0] = cm_nxt[0];
       cm_cur[1] = cm_nxt[1];
@@ -552,7 +603,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       d2 = d3;
       d3 = d4;
       ksc_nxt = ksc_n2;
-      wait_all_but_slot(j + 2);
+      wait_vmcnt<KI + VI>();  // slot j+1 has landed (only slot j+2's loads may be in flight)
       __syncthreads();
     };
     // last tile (slot n-1, buffer n % 3): P.V only.  One instantiation with a runtime buffer, so
@@ -567,8 +618,10 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         }
         f32x16 dummy[2];
         bf16x8 p_1[2][2], p_unused[2][2];
-        half_step(std::false_type(), std::true_type(), nullptr, 0, dummy, sv, 0, p_a, s_a, cm_cur, p_1);
-        half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, p_unused);
+        half_step(std::false_type(), std::true_type(), nullptr, 0, dummy, sv, 0, p_a, s_a, cm_cur, p_1,
+                  std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
+        half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, p_unused,
+                  std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
       }
     };
     for (int j = 0;;) {
@@ -580,6 +633,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       step(std::integral_constant<int, 0>(), j++);
     }
     last(n % NBUF);
+    wait_vmcnt<0>();  // the fills issued past the segment's end land before the ring is reused
     __syncthreads();  // the ring is refilled by the next pass or segment
 
     // Could some P have overflowed?  Decided for the whole workgroup, so that every wave runs the

@@ -241,6 +241,13 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
           per_wg[w].push_back(static_cast<int>(segs.size()) - 1);
         }
       }
+      // A range is the tail of one item followed by the heads of the next ones.  Running the
+      // tail last makes every workgroup start at key tile 0 of its first segment, so that the
+      // workgroups of one head walk the keys side by side (the tails, all of about the same
+      // length, run at one common offset) instead of at scattered offsets.
+      for (auto& v : per_wg) {
+        std::stable_partition(v.begin(), v.end(), [&](int k) { return segs[k].kt0 == 0; });
+      }
       int64_t worst = 0;
       for (auto& v : per_wg) {
         int64_t c = 0;
