@@ -157,16 +157,15 @@ struct TileLoader {
   }
 };
 
-// The VALU work that turns 32 scores per lane (2 query blocks x 16 keys) into bf16 P and the row
-// sums, as 112 operations in a software-pipelined order: for element e, F(e) = fma(s, c, -m),
-// X(e) = exp2, per pair of elements C = convert to bf16x2, and A(e) = add the bf16-rounded weight
-// (unpacked from its pair) to the row sum, so that the weights that multiply V sum exactly to the
-// normaliser.  Each operation depends only on operations at least two places earlier in the
-// list, so any run of consecutive operations can be issued between two MFMAs without waiting on
-// each other.  (The row sum uses v_add_f32 rather than v_dot2 on the bf16 pairs: v_dot2
-// instructions do not issue while an MFMA is executing.)
-enum : int { OP_F = 0, OP_X = 1, OP_C = 2, OP_A = 3 };
-constexpr int kValuOps = 112;
+// The VALU work that turns 32 scores per lane (2 query blocks x 16 keys) into bf16 P, as 80
+// operations in a software-pipelined order: for element e, F(e) = fma(s, c, -m), X(e) = exp2, and
+// per pair of elements C = convert to bf16x2.  Each operation depends only on operations at least
+// two places earlier in the list, so any run of consecutive operations can be issued between two
+// MFMAs without waiting on each other.  The row sums are taken separately, over the same
+// bf16-rounded weights (so that the weights that multiply V sum exactly to the normaliser), with
+// v_dot2 after the step's MFMAs: v_dot2 instructions do not issue while an MFMA is executing.
+enum : int { OP_F = 0, OP_X = 1, OP_C = 2 };
+constexpr int kValuOps = 80;
 struct ValuProgram {
   int kind[kValuOps], idx[kValuOps];
   constexpr ValuProgram() : kind(), idx() {
@@ -175,7 +174,6 @@ struct ValuProgram {
       if (s < 32) { kind[n] = OP_F; idx[n] = s; ++n; }
       if (s >= 1 && s <= 32) { kind[n] = OP_X; idx[n] = s - 1; ++n; }
       if (s >= 3 && (s & 1) && (s - 3) / 2 < 16) { kind[n] = OP_C; idx[n] = (s - 3) / 2; ++n; }
-      if (s >= 4) { kind[n] = OP_A; idx[n] = s - 4; ++n; }
     }
   }
 };
@@ -376,11 +374,24 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       st.t[e] = fmaf(s[e >> 4][e & 15], cm[e >> 4], -m[e >> 4]);
     } else if constexpr (kind == OP_X) {
       st.t[e] = fast_exp2(st.t[e]);
-    } else if constexpr (kind == OP_C) {
-      st.pw[e] = pack2_bf16(st.t[2 * e], st.t[2 * e + 1]);
     } else {
-      const uint32_t w = st.pw[e >> 1];
-      l[e >> 4] += __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+      st.pw[e] = pack2_bf16(st.t[2 * e], st.t[2 * e + 1]);
+    }
+  };
+  const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
+  // l += the sum of one half's bf16 weights (two partial chains per block: v_dot2 latency)
+  auto row_sums = [&](const bf16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 0, 1), ones2, a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 2, 3), ones2, a1, false);
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 4, 5), ones2, a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 6, 7), ones2, a1, false);
+      }
+      l[qb] += a0 + a1;
     }
   };
   auto anchor_l = [&]() { asm volatile("" ::"v"(l[0]), "v"(l[1])); };
@@ -399,6 +410,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     ValuState st;
     static_for<0, kValuOps>([&](auto kc) { valu_op(kc, st, s, cm); });
     p_operands(st, pb);
+    row_sums(pb);
   };
 
   // One half step.  MFMAs: (if HAS_S) the scores of half kb_next from K buffer sk into s_next, and
@@ -590,6 +602,9 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         // B: scores of tile j+1 half 1; P.V of tile j half 1; P of tile j+1 half 0
         half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, p_a,
                   std::integral_constant<int, VI>(), fvo, fvl, fvb);
+        __builtin_amdgcn_sched_barrier(0);
+        row_sums(p_1);
+        row_sums(p_a);
       } else {  // a wave without query rows still does its share of the fills
 #pragma unroll
         for (int i = 0; i < KI; ++i) Loader::dma16(fkl + 1024 * i, fko[i], fkb);
@@ -622,6 +637,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
                   std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
         half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, p_unused,
                   std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
+        row_sums(p_1);
       }
     };
     for (int j = 0;;) {
