@@ -188,6 +188,17 @@ __host__ __device__ constexpr int region_index(int r, int ns, int np) {  // inde
   for (int i = 0; i < r; ++i) k += region_is_s(i, ns, np) == region_is_s(r, ns, np);
   return k;
 }
+// VALU operations issued up to the start of region r, in proportion to the MFMA cycles of the
+// regions before it (a score MFMA lasts ws times as long as a P.V MFMA: 2 for e4m3, 1 for bf16)
+__host__ __device__ constexpr int valu_ops_before(int r, int ns, int np, int ws, int nops) {
+  int w = 0, tot = 0;
+  for (int i = 0; i < ns + np; ++i) {
+    const int wi = region_is_s(i, ns, np) ? ws : 1;
+    if (i < r) w += wi;
+    tot += wi;
+  }
+  return (w * nops) / tot;
+}
 // first region that uses K operand ks (score MFMA 2*ks) or V operand t (P.V MFMA 2*t)
 __host__ __device__ constexpr int k_first_use(int ks, int ns, int np) {
   for (int r = 0; r < ns + np; ++r)
@@ -464,8 +475,13 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         constexpr int dj = decltype(dc)::value;
         if constexpr (((2 * dj + 1) * NR) / (2 * ND) == r) Loader::dma16(dlds + 1024 * dj, doff[dj], dbase);
       });
-      if constexpr (HP) static_for<(r * kValuOps) / NR, ((r + 1) * kValuOps) / NR>([&](auto kc) { valu_op(kc, st, s_src, cm); });
       if constexpr (r + LA < NR) load_for(std::integral_constant<int, r + LA>());
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HP) {
+        constexpr int WS = FP8 ? 2 : 1;
+        static_for<valu_ops_before(r, NS, NP, WS, kValuOps), valu_ops_before(r + 1, NS, NP, WS, kValuOps)>(
+            [&](auto kc) { valu_op(kc, st, s_src, cm); });
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (HP) {
