@@ -95,32 +95,20 @@ struct TileLoader {
   }
 
   __device__ __forceinline__ void init(int head, int H) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    wave_u = __builtin_amdgcn_readfirstlane(wave);
-#pragma unroll
-    for (int j = 0; j < KI; ++j) koff[j] = k_src(wave, j, lane, BN, head, H);
-#pragma unroll
-    for (int j = 0; j < VI; ++j) voff[j] = v_src(wave, j, lane, BN, head, H);
+    wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    set_k(BN, head, H);
+    set_v(BN, head, H);
   }
 
-  // Per-lane source offsets of this wave's loads for a tile with nvalid valid keys.
-  __device__ __forceinline__ void k_offsets(int nvalid, int head, int H, uint32_t (&o)[KI]) const {
-    if (nvalid == BN) {
+  // koff / voff for a tile with nvalid valid keys (a chunk's last tile), in place; set_*(BN)
+  // restores the full-tile offsets.
+  __device__ __forceinline__ void set_k(int nvalid, int head, int H) {
 #pragma unroll
-      for (int j = 0; j < KI; ++j) o[j] = koff[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < KI; ++j) o[j] = k_src(wave_u, j, threadIdx.x & 63, nvalid, head, H);
-    }
+    for (int j = 0; j < KI; ++j) koff[j] = k_src(wave_u, j, threadIdx.x & 63, nvalid, head, H);
   }
-  __device__ __forceinline__ void v_offsets(int nvalid, int head, int H, uint32_t (&o)[VI]) const {
-    if (nvalid == BN) {
+  __device__ __forceinline__ void set_v(int nvalid, int head, int H) {
 #pragma unroll
-      for (int j = 0; j < VI; ++j) o[j] = voff[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < VI; ++j) o[j] = v_src(wave_u, j, threadIdx.x & 63, nvalid, head, H);
-    }
+    for (int j = 0; j < VI; ++j) voff[j] = v_src(wave_u, j, threadIdx.x & 63, nvalid, head, H);
   }
 
   // The fills are inline asm so that the compiler does not treat them as LDS stores: it would
@@ -236,7 +224,6 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const bool wave_active = 64 * wave < q_rows;
   const int n = kt1 - kt0;
-  const int rot_of_segment = p.rot_delta > 0 ? ((q_row0 / BM) * p.rot_delta) % n : 0;
 
   Loader ld;
   ld.init(head, H);
@@ -390,7 +377,9 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     }
   };
   const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
-  // l += the sum of one half's bf16 weights (two partial chains per block: v_dot2 latency)
+  // l += the sum of one half's bf16 weights (two v_dot2 chains per block: their latency).  Pairs
+  // are taken with whole-vector shuffles: this compiler folds word extracts from a bit-cast
+  // vector wrongly.
   auto row_sums = [&](const bf16x8 (&pb)[2][2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -496,14 +485,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   // ---- the key loop ------------------------------------------------------------------------
   // Ring: slot s (s >= -1) holds K of tile s+1 and V of tile s, in buffer (s+1) % 3.  Iteration j
   // reads slot j (scores of tile j+1, P.V of tile j) and fills slot j+2.
-  // The segment's tiles are visited from position `rot` on, wrapping around (softmax does not
-  // depend on the key order).  Staggering the start of the query tiles of one head lets the
-  // later ones find each K/V tile already in the XCD's L2.
-  const int rot = rot_of_segment;
-  auto tix = [&](int j) {  // absolute index of the j-th visited tile
-    const int r = j + rot;
-    return 2 * (kt0 + (r < n ? r : r - n));
-  };
+  auto tix = [&](int j) { return 2 * (kt0 + j); };  // descriptor of the segment's j-th tile
   // Tile descriptors (first pool row, valid keys) are read with scalar loads one step before
   // they are needed, so no step waits on a scalar load.
   struct Desc {
@@ -586,9 +568,9 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       // the segment's end the descriptors point at pool row 0, so every step issues the same
       // number of (in-bounds) loads and the wait below is a constant
       constexpr int FB = (B + 2) % NBUF;
-      uint32_t fko[KI], fvo[VI];
-      ld.k_offsets(d3.nv, head, H, fko);
-      ld.v_offsets(d2.nv, head, H, fvo);
+      const bool k_ragged = d3.nv < BN, v_ragged = d2.nv < BN;  // rare: a chunk's last tile
+      if (k_ragged) ld.set_k(d3.nv, head, H);
+      if (v_ragged) ld.set_v(d2.nv, head, H);
       const uint8_t* fkb = kpool + (size_t)d3.row0 * H * Loader::KB;
       const uint8_t* fvb = vpool + (size_t)d2.row0 * H * 2 * D;
       const uint32_t fkl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[FB] + ld.wave_u * KI * 1024;
@@ -610,23 +592,25 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         f32x16 s_n0[2];
         bf16x8 p_1[2][2];
         half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, p_1,
-                  std::integral_constant<int, KI>(), fko, fkl, fkb);
+                  std::integral_constant<int, KI>(), ld.koff, fkl, fkb);
         if (nv_nxt < BN) {
           score_drain(s_n0);
           mask_half(s_n0, 0, nv_nxt);
         }
         // B: scores of tile j+1 half 1; P.V of tile j half 1; P of tile j+1 half 0
         half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, p_a,
-                  std::integral_constant<int, VI>(), fvo, fvl, fvb);
+                  std::integral_constant<int, VI>(), ld.voff, fvl, fvb);
         __builtin_amdgcn_sched_barrier(0);
         row_sums(p_1);
         row_sums(p_a);
       } else {  // a wave without query rows still does its share of the fills
 #pragma unroll
-        for (int i = 0; i < KI; ++i) Loader::dma16(fkl + 1024 * i, fko[i], fkb);
+        for (int i = 0; i < KI; ++i) Loader::dma16(fkl + 1024 * i, ld.koff[i], fkb);
 #pragma unroll
-        for (int i = 0; i < VI; ++i) Loader::dma16(fvl + 1024 * i, fvo[i], fvb);
+        for (int i = 0; i < VI; ++i) Loader::dma16(fvl + 1024 * i, ld.voff[i], fvb);
       }
+      if (k_ragged) ld.set_k(BN, head, H);
+      if (v_ragged) ld.set_v(BN, head, H);
       cm_cur[0] = cm_nxt[0];
       cm_cur[1] = cm_nxt[1];
       nv_cur = nv_nxt;

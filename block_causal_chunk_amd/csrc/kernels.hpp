@@ -24,7 +24,6 @@ struct FwdParams {
   float c;                 // softmax scale * log2(e)
   float scale;             // softmax scale
   uint32_t nonce_lo, nonce_hi;
-  int32_t rot_delta;       // tiles by which consecutive query tiles' key loops are staggered
 };
 
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s);
