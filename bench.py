@@ -44,8 +44,8 @@ def kernel_src_hash() -> str:
 
 
 def traffic_from_profiles(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken with the
-    current kernel sources; else None."""
+    """Beyond-L2 bytes per call (attention + merge launches) from the committed rocprofv3 counter
+    summary, if it was taken with the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.json")
     if not os.path.exists(p):
         return None
@@ -55,7 +55,7 @@ def traffic_from_profiles(workload: str):
         return None
     if d.get("kernel_src_sha") != kernel_src_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
