@@ -93,8 +93,8 @@ def cpu_baseline(case, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="wan13b_task")
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=0)
