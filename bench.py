@@ -36,6 +36,29 @@ def effective_flops(table) -> float:
     return 4.0 * t.head_dim * t.num_heads * tot
 
 
+def gather_bytes(table, k_bytes: int) -> tuple:
+    """(K/V bytes staged into LDS per call, unique visible K/V bytes per call).  Every query tile of
+    up to 256 rows of one head loads the 64-key tiles of its visible prefix (a tile never crosses a
+    page), K at k_bytes and V at 2 bytes per element."""
+    t = table
+    d, H = t.head_dim, t.num_heads
+    tiles = []
+    for c in range(t.num_chunks):
+        tok = int(t.chunk_tokens[c])
+        n = 0
+        for p0 in range(0, tok, t.page_size):
+            n += -(-min(t.page_size, tok - p0) // 64)
+        tiles.append(n)
+    staged = 0
+    visible = set()
+    for a in t.query_chunks:
+        pre = [b for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a]]
+        visible.update(pre)
+        staged += H * -(-int(t.chunk_tokens[a]) // 256) * sum(tiles[b] for b in pre) * 64 * d * (k_bytes + 2)
+    unique = sum(int(t.chunk_tokens[b]) for b in visible) * H * d * (k_bytes + 2)
+    return staged, unique
+
+
 def kernel_src_hash() -> str:
     h = hashlib.sha256()
     for f in ["attn_fwd.hip", "device.hpp", "plan.cpp", "plan.hpp"]:
@@ -56,6 +79,21 @@ def traffic_from_profiles(workload: str):
     if d.get("kernel_src_sha") != kernel_src_hash():
         return None
     return d.get("hbm_bytes_per_call")
+
+
+def mfma_counters_from_profiles(workload: str):
+    """MFMA busy fraction, VALU co-issue share and active clock of the attention kernel from the
+    committed rocprofv3 counter summary, if it was taken with the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_mfma_util.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("kernel_src_sha") != kernel_src_hash():
+        return None
+    return {k: d[k] for k in ("mfma_busy_frac", "valu_coexec_frac_of_mfma_busy", "active_clock_ghz")}
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -187,6 +225,12 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     tasks = len(t.query_chunks) / (ms * 1e-3)
     peak = PEAK_MIXED if fp8 else PEAK_BF16
+    staged, unique = gather_bytes(t, 1 if fp8 else 2)
+    traffic = traffic_from_profiles(args.workload)
+    sec = ms * 1e-3
+    gather = {"lds_staged_bytes": staged, "lds_staged_gbs": round(staged / sec / 1e9, 1),
+              "kv_unique_bytes": unique, "kv_unique_gbs": round(unique / sec / 1e9, 1),
+              "beyond_l2_gbs": None if traffic is None else round(traffic / sec / 1e9, 1)}
     res = {
         "metric": "effective attention TFLOP/s (unmasked pairs only) + chunk-tasks/s, % of MFMA peak",
         "value": round(tflops, 2),
@@ -213,7 +257,9 @@ def main():
         "plan": {"items": int(summary[0]), "key_tiles": int(summary[1]), "merge_groups": int(summary[2]),
                  "splits": int(summary[6]), "block_m": int(summary[4]), "block_n": int(summary[5])},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic_from_profiles(args.workload)},
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "mfma_counters": mfma_counters_from_profiles(args.workload),
+        "gather": gather,
         "wall_s_timed": round(wall, 3),
     }
     if fp8:
