@@ -41,7 +41,7 @@ class ChunkTableC(ctypes.Structure):
 
 class OptsC(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
+                ("order_ties", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
 
 
 _lib = None
@@ -148,9 +148,9 @@ def make_table_c(table):
     return c, arrs
 
 
-def wfattn_plan(table, split_k: int = 0, xcd_remap: int = 0) -> Plan:
+def wfattn_plan(table, split_k: int = 0, xcd_remap: int = 0, order_ties: int = 0) -> Plan:
     c, keep = make_table_c(table)
-    o = OptsC(int(split_k), int(xcd_remap), 0, 0)
+    o = OptsC(int(split_k), int(xcd_remap), int(order_ties), 0)
     h = ctypes.c_void_p()
     _check(lib().wfattn_plan(ctypes.byref(c), ctypes.byref(o), ctypes.byref(h)), "wfattn_plan")
     del keep
@@ -185,10 +185,10 @@ class Attention:
     """A plan plus its uploaded workspace on one device; call() runs one forward."""
 
     def __init__(self, table, device="cuda", mode: int = WFATTN_WS_BF16, split_k: int = 0, xcd_remap: int = 0,
-                 stream=None):
+                 stream=None, order_ties: int = 0):
         import torch
         self.table = table
-        self.plan = wfattn_plan(table, split_k=split_k, xcd_remap=xcd_remap)
+        self.plan = wfattn_plan(table, split_k=split_k, xcd_remap=xcd_remap, order_ties=order_ties)
         self.mode = mode
         nbytes = self.plan.workspace_bytes(mode)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

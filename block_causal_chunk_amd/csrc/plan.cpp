@@ -31,7 +31,7 @@ struct Seg {
   int32_t item, kt0, kt1, slot;
 };
 
-wfattn_status validate(const wfattn_chunk_table* t) {
+wfattn_status validate(const wfattn_chunk_table* t, bool ties) {
   if (!t->chunk_tokens || !t->chunk_order || !t->page_offsets || !t->page_ids || !t->query_chunks)
     return WFATTN_ERR_NULL;
   if (t->num_chunks < 1 || t->num_heads < 1 || t->num_query_chunks < 1 || t->page_size < 1 ||
@@ -45,7 +45,7 @@ wfattn_status validate(const wfattn_chunk_table* t) {
   for (int c = 0; c < n; ++c) {
     if (t->chunk_tokens[c] < 1) return WFATTN_ERR_INVALID;
     const int o = t->chunk_order[c];
-    if (o < 0 || o >= n || seen[o]) return WFATTN_ERR_INVALID;  // not a permutation
+    if (o < 0 || o >= n || (seen[o] && !ties)) return WFATTN_ERR_INVALID;  // not a permutation
     seen[o] = 1;
   }
   if (t->page_offsets[0] != 0) return WFATTN_ERR_INVALID;
@@ -113,10 +113,10 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
   if (!table || !plan_out) return WFATTN_ERR_NULL;
   wfattn_opts o{};
   if (opts) o = *opts;
-  if (o.reserved0 != 0 || o.reserved1 != 0 || o.split_k < 0 || o.split_k > 64 ||
+  if (o.order_ties < 0 || o.order_ties > 1 || o.reserved1 != 0 || o.split_k < 0 || o.split_k > 64 ||
       o.xcd_remap < -1 || o.xcd_remap > 1)
     return WFATTN_ERR_UNSUPPORTED;
-  wfattn_status st = validate(table);
+  wfattn_status st = validate(table, o.order_ties == 1);
   if (st != WFATTN_OK) return st;
 
   wfattn_plan_s* ps = new (std::nothrow) wfattn_plan_s();
@@ -136,9 +136,13 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
                                          : static_cast<float>(1.0 / std::sqrt((double)table->head_dim));
     P.xcd_remap = (o.xcd_remap == -1) ? 0 : 1;
 
-    // Key tiles of all chunks, clean -> noisy; prefix_end[c] = tiles up to and including c.
+    // Key tiles of all chunks, clean -> noisy (chunks of equal order by index); prefix_end[c] =
+    // tiles up to and including the last chunk whose order is not above c's, so the visible keys
+    // of every query chunk are a prefix of this list.
     std::vector<int> by_order(n);
-    for (int c = 0; c < n; ++c) by_order[table->chunk_order[c]] = c;
+    std::iota(by_order.begin(), by_order.end(), 0);
+    std::stable_sort(by_order.begin(), by_order.end(),
+                     [&](int x, int y) { return table->chunk_order[x] < table->chunk_order[y]; });
     std::vector<int32_t> tiles;
     std::vector<int32_t> prefix_end(n, 0);
     for (int r = 0; r < n; ++r) {
@@ -155,6 +159,9 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
       }
       prefix_end[c] = static_cast<int32_t>(tiles.size() / kTileInts);
     }
+    for (int r = n - 2; r >= 0; --r)  // a tie group ends where its last member ends
+      if (table->chunk_order[by_order[r]] == table->chunk_order[by_order[r + 1]])
+        prefix_end[by_order[r]] = prefix_end[by_order[r + 1]];
     P.n_tiles = static_cast<int32_t>(tiles.size() / kTileInts);
 
     // Items: (query chunk, query tile of up to kBlockM rows, head) with the whole visible prefix.
@@ -439,4 +446,4 @@ extern "C" const char* wfattn_status_str(wfattn_status s) {
   return "unknown status";
 }
 
-extern "C" int32_t wfattn_abi_version(void) { return 1; }
+extern "C" int32_t wfattn_abi_version(void) { return 2; }

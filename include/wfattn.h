@@ -47,7 +47,8 @@ extern "C" {
 typedef enum wfattn_status {
   WFATTN_OK = 0,
   WFATTN_ERR_NULL = 1,        /* a required pointer is NULL                                    */
-  WFATTN_ERR_INVALID = 2,     /* malformed table: token count < 1, order not a permutation,   */
+  WFATTN_ERR_INVALID = 2,     /* malformed table: token count < 1, order not a permutation    */
+                              /* (with ties allowed: an order outside [0, num_chunks)),       */
                               /* page count != ceil(tokens/page_size), duplicate or unknown   */
                               /* query chunk, heads < 1, bad plan handle                      */
   WFATTN_ERR_RANGE = 3,       /* page id out of range or used twice; a size overflows int32   */
@@ -75,8 +76,10 @@ typedef struct wfattn_chunk_table {
   const int32_t* chunk_tokens;  /* [num_chunks], each >= 1                                      */
   const int32_t* chunk_order;   /* [num_chunks], a permutation of 0..num_chunks-1; 0 = cleanest */
                                 /* (oldest).  Key chunk b is visible to query chunk a iff       */
-                                /* chunk_order[b] <= chunk_order[a].  A strict order: a tie     */
-                                /* would be a two-way edge, which the method removes.           */
+                                /* chunk_order[b] <= chunk_order[a].  A strict order by default: */
+                                /* a tie would be a two-way edge, which the method removes.     */
+                                /* With wfattn_opts.order_ties = 1, values in [0, num_chunks)   */
+                                /* may repeat and chunks of equal order see each other.         */
   const int32_t* page_offsets;  /* [num_chunks+1], CSR into page_ids; chunk c owns exactly      */
                                 /* ceil(chunk_tokens[c]/page_size) pages, token u of chunk c is */
                                 /* in page page_ids[page_offsets[c] + u/page_size], slot        */
@@ -100,7 +103,12 @@ typedef struct wfattn_opts {
                      /* range; n > 1: cut every item's key range into up to n parts; parts are  */
                      /* merged through their LSEs                                                */
   int32_t xcd_remap; /* 0: default (on); 1: on; -1: off.  Groups one head's work on one XCD     */
-  int32_t reserved0; /* must be 0 */
+  int32_t order_ties; /* 0: chunk_order must be a permutation (the directed frontier: a later,  */
+                      /* noisier chunk is never visible).  1: equal orders allowed; chunks of  */
+                      /* one order form a window that attends to itself both ways (the live    */
+                      /* bidirectional window of Rolling Forcing, Wave Forcing project page,   */
+                      /* "01 - The design gap", column "A - Live frontier"), while every       */
+                      /* cleaner order stays one-way.  Other values: UNSUPPORTED.              */
   int32_t reserved1; /* must be 0 */
 } wfattn_opts;
 
@@ -181,7 +189,7 @@ wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t head
 /* Static string naming a status. */
 const char* wfattn_status_str(wfattn_status status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2 gave wfattn_opts.order_ties its meaning; it had to be 0). */
 int32_t wfattn_abi_version(void);
 
 #ifdef __cplusplus

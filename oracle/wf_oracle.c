@@ -16,9 +16,11 @@
  *    into their final slots and the consumer reads them where they lie.
  *  - project page, "03 - End-to-end KV transport", panel "03 - Layout": each producer owns a fixed
  *    slot in the consumer's buffer and attention reads the prefix in place.
- *  Reading taken where the pages are silent: "earlier/cleaner" is a strict total order given by
- *  chunk_order (smaller = cleaner); key chunk b is visible to query chunk a iff
- *  order[b] <= order[a]; b == a is always visible (full attention inside the chunk).
+ *  Reading taken where the pages are silent: "earlier/cleaner" is the order given by chunk_order
+ *  (smaller = cleaner); key chunk b is visible to query chunk a iff order[b] <= order[a]; b == a
+ *  is always visible (full attention inside the chunk).  Equal orders (allowed only where the
+ *  caller asks for them) make those chunks see each other both ways, the live bidirectional
+ *  window of Rolling Forcing (project page, "01 - The design gap", column "A - Live frontier").
  *
  * The attention is the textbook two-pass softmax: s_j = scale * <q, k_j>, m = max_j s_j,
  * Z = sum_j exp(s_j - m), o = sum_j exp(s_j - m) / Z * v_j, lse = m + log Z.  No tiling, no

@@ -115,6 +115,63 @@ def test_degenerate_tables(B, O):
             assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
 
 
+# ------------------------------------------------------------------ mask variants
+def _poison_chunks(c, chunks):
+    """NaN into every pool slot of `chunks`: keys the mask must never read."""
+    t = c.table
+    for b in chunks:
+        pages = t.page_ids[t.page_offsets[b]:t.page_offsets[b + 1]]
+        idx = torch.from_numpy(np.asarray(pages, np.int64))
+        c.k_pool[idx] = float("nan")
+        c.v_pool[idx] = float("nan")
+
+
+def test_tied_window(B, O):
+    """Equal chunk orders (wfattn_opts.order_ties = 1): a sink and two history chunks, then three
+    active chunks of one order that see each other both ways (Rolling Forcing's live window), then
+    a noisier chunk whose K/V are NaN; the window's chunks are the queries, listed out of order.
+    Uneven chunk sizes, ragged query and key tiles."""
+    rng = np.random.default_rng(41)
+    for tok, page, H, d in [([64, 100, 37, 96, 130, 70, 90], 64, 2, 128),
+                            ([300, 280, 300, 310, 260, 300, 300], 256, 3, 128),
+                            ([40, 40, 40, 40, 40, 40, 40], 64, 2, 64)]:
+        order = [0, 1, 2, 3, 3, 3, 4]
+        t = make_table(tok, order, [5, 3, 4], page, H, d, shuffle_rng=rng, spare=2)
+        c = fill_case("tied", t, rng, torch.bfloat16)
+        _poison_chunks(c, [6])
+        ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+        q, k, v = to_dev(c)
+        for split in (1, 0, 3):
+            print(f"[case] tied window {tok} page={page} H={H} d={d} split_k={split}", flush=True)
+            att = B.Attention(t, split_k=split, order_ties=1)
+            out, lse = att.fwd(q, k, v, want_lse=True)
+            torch.cuda.synchronize()
+            assert np.isfinite(f64(out)).all()
+            check_bf16(f64(out), ref, "tied")
+            assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+
+
+def test_store_rank_query_shape(B, O):
+    """The store step re-runs the finished chunk over its clean context: the query is the store
+    chunk (after a sink and a clean history), while four noisier chunks still in flight sit in the
+    pool with NaN K/V and must never be read (KipQuest page, "The deep dive"; project page, "02 -
+    Interactive pipeline": the store and the other cleaner producers have the shorter legal
+    context)."""
+    rng = np.random.default_rng(43)
+    tok = [64, 4680, 4680, 4680, 4680, 4680, 4680, 4680]
+    order = [0, 1, 2, 3, 4, 5, 6, 7]
+    t = make_table(tok, order, [3], 256, 4, 128, shuffle_rng=rng, spare=1)
+    c = fill_case("store", t, rng, torch.bfloat16)
+    _poison_chunks(c, [4, 5, 6, 7])
+    print("[case] store-rank query shape", flush=True)
+    out, lse, _ = run(B, c)
+    assert np.isfinite(f64(out)).all()
+    rows = sample_rows(t.lq, n=48)
+    ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool, rows=rows)
+    check_bf16(f64(out)[rows], ref, "store")
+    assert np.abs(f64(lse).T[rows] - ref_lse).max() <= LSE_TOL
+
+
 # ------------------------------------------------------------------ invariants (bitwise)
 def test_page_shuffle_is_bitwise_identical(B):
     c = medium_case("long_rollout", seed=5)

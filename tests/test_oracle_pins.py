@@ -3,7 +3,8 @@
 P1 dense explicit mask, P2 a library routine (torch SDPA in float64), P3 the single-chunk special
 case, P4 closed forms, P5 permutation/page-shuffle invariance, P6 no reverse edge, P7
 decomposition of a multi-chunk query set, P8 the e4m3 codec against the OCP definition and
-torch's float8_e4m3fn, P9 merging key partitions through their LSEs, plus brute force on tiny
+torch's float8_e4m3fn, P9 merging key partitions through their LSEs, P10 ties in chunk order (full
+attention when all tie, a tie group equals one merged chunk, SDPA), plus brute force on tiny
 inputs, a hand-derived closed-form fixture, and checks that plausible mistakes would be caught.
 """
 import json
@@ -89,6 +90,63 @@ def test_p2_sdpa_float64(oracle_lib, seed):
     s = (q @ keys.permute(1, 2, 0)) / math.sqrt(d)
     s = s.masked_fill(~mask, float("-inf"))
     assert np.abs(l - torch.logsumexp(s, dim=-1).T.numpy()).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- P10: ties in chunk order
+# Chunks of equal order see each other both ways (the live bidirectional window of Rolling
+# Forcing, Wave Forcing project page, "01 - The design gap", column "A - Live frontier"); the rule
+# order[b] <= order[a] is unchanged.
+def test_p10_all_tied_is_full_attention(oracle_lib):
+    rng = np.random.default_rng(11)
+    H, d, tokens = 2, 32, [9, 14, 6, 11]
+    c = _contiguous_case(rng, tokens, [0, 0, 0, 0], [0, 1, 2, 3], H, d)
+    o, l = oracle_lib.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    q = c.q.double().transpose(0, 1)
+    k = c.k_pool.double()[:, 0].transpose(0, 1)
+    v = c.v_pool.double()[:, 0].transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)  # no mask at all
+    assert np.abs(o - ref.transpose(0, 1).numpy()).max() <= 1e-12
+    s = (q @ k.transpose(1, 2)) / math.sqrt(d)
+    assert np.abs(l - torch.logsumexp(s, dim=-1).T.numpy()).max() <= 1e-12
+
+
+def test_p10_tie_group_equals_one_merged_chunk(oracle_lib):
+    """Two tied chunks behave as one chunk holding both token sets: a table with the strict order
+    the other pins cover gives the same outputs."""
+    rng = np.random.default_rng(12)
+    H, d = 2, 16
+    tied = _contiguous_case(rng, [20, 17, 23, 11], [0, 1, 1, 2], [1, 2], H, d)
+    merged = make_table([20, 40, 11], [0, 1, 2], [1], 1, H, d, shuffle_rng=None, spare=0)
+    # page_size 1 and identity page tables: pool rows are the tokens chunk by chunk in both tables
+    o_t, l_t = oracle_lib.attn_rows(tied.table, tied.q, tied.k_pool, tied.v_pool)
+    o_m, l_m = oracle_lib.attn_rows(merged, tied.q, tied.k_pool, tied.v_pool)
+    assert np.abs(o_t - o_m).max() <= 1e-13 and np.abs(l_t - l_m).max() <= 1e-13
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_p10_ties_sdpa_and_dense(oracle_lib, seed):
+    from oracle.dense import attn_dense
+    rng = np.random.default_rng(200 + seed)
+    tokens = list(rng.integers(5, 25, size=6))
+    order = [0, 1, 2, 2, 2, 3]
+    queries = [4, 2, 5, 3]
+    H, d = 2, 32
+    c = _contiguous_case(rng, tokens, order, queries, H, d)
+    o, l = oracle_lib.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    keys, vals = c.k_pool.double()[:, 0], c.v_pool.double()[:, 0]
+    mask = _sdpa_mask(tokens, order, queries)
+    q = c.q.double().transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, keys.transpose(0, 1), vals.transpose(0, 1), attn_mask=mask)
+    assert np.abs(o - ref.transpose(0, 1).numpy()).max() <= 1e-12
+    od, ld = attn_dense(c.table, c.q, c.k_pool, c.v_pool)
+    assert np.abs(o - od).max() <= 1e-13 and np.abs(l - ld).max() <= 1e-13
+    # the window really is two-way: the first query of chunk 4 sees chunk 2's keys, the first
+    # query of chunk 2 (rows after chunk 4's) sees chunk 4's keys, and neither sees chunk 5
+    m = mask.numpy()
+    k2, k4, k5 = sum(tokens[:2]), sum(tokens[:4]), sum(tokens[:5])
+    assert m[0, k2:k2 + tokens[2]].all() and m[tokens[4], k4:k4 + tokens[4]].all()
+    assert not m[0, k5:].any() and not m[tokens[4], k5:].any()
 
 
 # ---------------------------------------------------------------- P3: single chunk

@@ -28,14 +28,14 @@ def test_exports_every_declared_symbol(B):
     L = B.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wfattn_abi_version() == 1
+    assert L.wfattn_abi_version() == 2
     for s in range(8):
         assert B.status_str(s) and B.status_str(s) != "unknown status"
 
 
 def _plan_status(B, t, **opts):
     c, keep = B.make_table_c(t)
-    o = B.OptsC(opts.get("split_k", 0), opts.get("xcd_remap", 0), opts.get("r0", 0), 0)
+    o = B.OptsC(opts.get("split_k", 0), opts.get("xcd_remap", 0), opts.get("order_ties", 0), opts.get("r1", 0))
     h = ctypes.c_void_p()
     st = B.lib().wfattn_plan(ctypes.byref(c), ctypes.byref(o), ctypes.byref(h))
     if st == 0:
@@ -82,7 +82,19 @@ def test_plan_errors(B):
     assert mod(head_dim=96) == B.WFATTN_ERR_UNSUPPORTED
     t = make_table([100, 70], [0, 1], [1], 32, 2, 128)  # page_size not a multiple of 64
     assert _plan_status(B, t) == B.WFATTN_ERR_UNSUPPORTED
-    assert _plan_status(B, _base(), r0=1) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), order_ties=2) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), order_ties=-1) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), r1=1) == B.WFATTN_ERR_UNSUPPORTED
+    # ties only where asked for; an order outside [0, num_chunks) stays invalid either way
+    t = _base()
+    t.chunk_order = np.array([0, 1, 1], np.int32)
+    assert _plan_status(B, t, order_ties=1) == B.WFATTN_OK
+    t.chunk_order = np.array([1, 1, 1], np.int32)
+    assert _plan_status(B, t, order_ties=1) == B.WFATTN_OK
+    t.chunk_order = np.array([0, 1, 3], np.int32)
+    assert _plan_status(B, t, order_ties=1) == B.WFATTN_ERR_INVALID
+    t.chunk_order = np.array([0, -1, 1], np.int32)
+    assert _plan_status(B, t, order_ties=1) == B.WFATTN_ERR_INVALID
     assert _plan_status(B, _base(), split_k=-1) == B.WFATTN_ERR_UNSUPPORTED
     assert _plan_status(B, _base(), xcd_remap=2) == B.WFATTN_ERR_UNSUPPORTED
     t = make_table([100], [0], [0], 64, 2, 128)
@@ -240,6 +252,25 @@ def test_schedule_random_tables(B):
                        int(rng.choice([64, 128, 256])), int(rng.integers(1, 4)), int(rng.choice([64, 128])),
                        shuffle_rng=rng, spare=int(rng.integers(0, 4)))
         _check_schedule(B, t, split_k=int(rng.integers(0, 5)))
+
+
+def test_schedule_random_tables_with_ties(B):
+    """Equal orders (a bidirectional window): every query chunk of a tie group sees the whole group
+    and every cleaner chunk, each key once, and never a noisier chunk."""
+    rng = np.random.default_rng(6)
+    for _ in range(10):
+        n = int(rng.integers(1, 8))
+        tok = rng.integers(1, 300, size=n)
+        order = rng.integers(0, max(1, n // 2) + 1, size=n).clip(0, n - 1)
+        t = make_table(tok, order, rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False),
+                       int(rng.choice([64, 128])), int(rng.integers(1, 3)), int(rng.choice([64, 128])),
+                       shuffle_rng=rng, spare=int(rng.integers(0, 3)))
+        _check_schedule(B, t, split_k=int(rng.integers(0, 4)), order_ties=1)
+    # a window of three tied chunks after a clean history: each window query tile gets the same prefix
+    t = make_table([100, 64, 200, 130, 90, 70], [0, 1, 2, 2, 2, 3], [4, 2, 3], 64, 1, 128)
+    plan, items, tiles = _check_schedule(B, t, order_ties=1)
+    assert len(set(int(it[5]) for it in items)) == 1
+    assert int(tiles[:int(items[0][5]), 1].sum()) == 100 + 64 + 200 + 130 + 90
 
 
 def test_schedule_full_size_tables_and_xcd_grouping(B):
