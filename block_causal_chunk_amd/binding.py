@@ -20,7 +20,9 @@ WFATTN_WS_BF16, WFATTN_WS_FP32, WFATTN_WS_FP8 = 0, 1, 2
 
 EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_workspace_bytes",
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
-            "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version"]
+            "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
+            "wfattn_fwd_gated"]
+WFATTN_GATE_SPIN_MAX = 1 << 20
 
 
 class WfattnError(RuntimeError):
@@ -73,6 +75,10 @@ def lib():
         L.wfattn_fwd_fp8.restype = i32
         L.wfattn_quantize_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.wfattn_quantize_fp8.restype = i32
+        L.wfattn_publish_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
+        L.wfattn_publish_kv.restype = i32
+        L.wfattn_fwd_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, vp, vp]
+        L.wfattn_fwd_gated.restype = i32
         L.wfattn_status_str.argtypes = [i32]
         L.wfattn_status_str.restype = ctypes.c_char_p
         L.wfattn_abi_version.argtypes = []
@@ -171,6 +177,19 @@ def wfattn_fwd_fp8(plan: Plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, 
     _check(lib().wfattn_fwd_fp8(plan.handle, _ptr(q8), _ptr(q_scale), _ptr(k8_pool), _ptr(k_scale), _ptr(v_pool),
                                 _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "wfattn_fwd_fp8")
+
+
+def wfattn_publish_kv(plan: Plan, chunk: int, k_src, v_src, k_pool, v_pool, flags, generation: int, ws, stream=None):
+    _check(lib().wfattn_publish_kv(plan.handle, int(chunk), _ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
+                                   _ptr(flags), int(generation) & 0xffffffff, _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "wfattn_publish_kv")
+
+
+def wfattn_fwd_gated(plan: Plan, q, k_pool, v_pool, out, lse, ws, flags, need, spin_limit: int, gate_status,
+                     stream=None):
+    _check(lib().wfattn_fwd_gated(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _ptr(flags), _ptr(need), int(spin_limit),
+                                  _ptr(gate_status), _stream(stream)), "wfattn_fwd_gated")
 
 
 def wfattn_quantize_fp8(x, rows: int, heads: int, head_dim: int, x8, scales, stream=None):

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwfattn.so")
-SOURCES = ["plan.cpp", "api.hip", "attn_fwd.hip", "quant.hip"]
+SOURCES = ["plan.cpp", "api.hip", "attn_fwd.hip", "quant.hip", "publish.hip"]
 ARCH = "gfx950"
 
 

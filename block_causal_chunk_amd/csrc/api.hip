@@ -40,8 +40,18 @@ extern "C" wfattn_status wfattn_plan_upload(const wfattn_plan_t* plan, void* ws,
   return e == hipSuccess ? WFATTN_OK : WFATTN_ERR_DEVICE;
 }
 
-extern "C" wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q, const void* k_pool,
-                                    const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+struct Gate {
+  const uint32_t* flags;
+  const uint32_t* need;
+  uint32_t* status;
+  int32_t spin;
+};
+
+wfattn_status fwd_impl(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q, const void* k_pool,
+                       const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                       const Gate* gate) {
   if (!plan || !q || !k_pool || !v_pool || !out) return WFATTN_ERR_NULL;
   if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
   if (dtype != WFATTN_BF16 && dtype != WFATTN_FP32) return WFATTN_ERR_UNSUPPORTED;
@@ -56,6 +66,12 @@ extern "C" wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtyp
   FwdParams fp = base_params(P, ws);
   fp.out = out;
   fp.lse = lse;
+  if (gate) {
+    fp.gate_flags = gate->flags;
+    fp.gate_need = gate->need;
+    fp.gate_status = gate->status;
+    fp.gate_spin = gate->spin;
+  }
   if (f32) {
     char* w = static_cast<char*>(ws);
     uint16_t* sq = reinterpret_cast<uint16_t*>(w + P->stage_q_off);
@@ -78,6 +94,52 @@ extern "C" wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtyp
   if (launch_attn_bf16(fp, P->head_dim, f32, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (launch_combine(fp, P->head_dim, f32, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   return WFATTN_OK;
+}
+
+}  // namespace
+
+extern "C" wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q, const void* k_pool,
+                                    const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_impl(plan, dtype, q, k_pool, v_pool, out, lse, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" wfattn_status wfattn_fwd_gated(const wfattn_plan_t* plan, const void* q, const void* k_pool,
+                                          const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes,
+                                          const uint32_t* flags, const uint32_t* need, int32_t spin_limit,
+                                          uint32_t* gate_status, void* stream) {
+  if (!flags || !need || !gate_status) return WFATTN_ERR_NULL;
+  if (spin_limit < 0 || spin_limit > WFATTN_GATE_SPIN_MAX) return WFATTN_ERR_RANGE;
+  if (!aligned(flags, 4) || !aligned(need, 4) || !aligned(gate_status, 4)) return WFATTN_ERR_UNSUPPORTED;
+  const Gate g{flags, need, gate_status, spin_limit};
+  return fwd_impl(plan, WFATTN_BF16, q, k_pool, v_pool, out, lse, ws, ws_bytes, stream, &g);
+}
+
+extern "C" wfattn_status wfattn_publish_kv(const wfattn_plan_t* plan, int32_t chunk, const void* k_src,
+                                           const void* v_src, void* k_pool, void* v_pool, uint32_t* flags,
+                                           uint32_t generation, const void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !k_src || !v_src || !k_pool || !v_pool) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  const Plan* P = as_plan(plan);
+  if (chunk < 0 || chunk >= P->num_chunks) return WFATTN_ERR_INVALID;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(flags, 4) || !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  PublishParams pp{};
+  pp.k_src = static_cast<const uint16_t*>(k_src);
+  pp.v_src = static_cast<const uint16_t*>(v_src);
+  pp.k_pool = static_cast<uint16_t*>(k_pool);
+  pp.v_pool = static_cast<uint16_t*>(v_pool);
+  pp.blob = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + P->ws_blob);
+  pp.chunk = chunk;
+  pp.row_granules = P->num_heads * P->head_dim * 2 / 16;
+  pp.nonce_lo = static_cast<uint32_t>(P->nonce & 0xffffffffu);
+  pp.nonce_hi = static_cast<uint32_t>(P->nonce >> 32);
+  pp.flags = flags;
+  pp.generation = generation;
+  const int64_t tokens = P->blob[P->off_chunks + static_cast<size_t>(chunk) * kChunkInts + 1];
+  return launch_publish(pp, tokens, static_cast<hipStream_t>(stream)) == hipSuccess ? WFATTN_OK : WFATTN_ERR_DEVICE;
 }
 
 extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,

@@ -211,7 +211,7 @@ __host__ __device__ constexpr int v_first_use(int t, int ns, int np) {
 // every P of the row; if some l reaches 2^64 (some score exceeded the first tile's max by more
 // than 44 natural-log units) the segment is recomputed against the true row max, found by a
 // score-only sweep, which no score exceeds.
-template <int D, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32, bool GATED>
 __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* items, int item, int kt0, int kt1,
                                             int slot, const int32_t* tiles,
                                             uint8_t (*smem_k)[BN * TileLoader<D, FP8>::KB], uint16_t (*smem_v)[BN * D],
@@ -221,7 +221,12 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   const int head = ld_const(items, item * kItemInts + 0), q_row0 = ld_const(items, item * kItemInts + 1);
   const int q_rows = ld_const(items, item * kItemInts + 2), qsb = ld_const(items, item * kItemInts + 3);
   const int H = p.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  // gated kernels: lane-dependent addressing is derived per segment (an opaque copy of the thread
+  // index keeps the compiler from hoisting it out of the segment loop, where next to the gate's
+  // registers it would spill)
+  int tid = threadIdx.x;
+  if constexpr (GATED) asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const bool wave_active = 64 * wave < q_rows;
   const int n = kt1 - kt0;
 
@@ -730,8 +735,42 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   }
 }
 
+// Gate of one work item: every chunk of rank 0 .. last (the item's visible chunks) must carry a
+// generation flag at least the one the caller needs.  Wave 0 polls with acquire loads (at most
+// gate_spin sleeps, so the wait always ends) and the decision is shared through LDS, so the whole
+// workgroup takes the same branch.  A chunk that is not ready skips the item and sets bit 0 of
+// the caller's status word.
+__device__ bool gate_item(const FwdParams& p, const int32_t* items, int item, int* decision) {
+  const int32_t* byrank = p.blob + ld_const(p.blob, H_OFF_BYRANK);
+  const int last = ld_const(items, item * kItemInts + 6);
+  if (threadIdx.x < 64) {
+    bool ready = false;
+    for (int it = 0;; ++it) {
+      bool mine = true;
+      for (int r = threadIdx.x; r <= last; r += 64) {
+        const int c = byrank[r];
+        const uint32_t f = __hip_atomic_load(p.gate_flags + c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        mine = mine && f >= p.gate_need[c];
+      }
+      ready = __all(mine);
+      if (ready || it >= p.gate_spin) break;
+      __builtin_amdgcn_s_sleep(63);
+    }
+    if (threadIdx.x == 0) {
+      *decision = ready ? 1 : 0;
+      if (!ready) atomicOr(p.gate_status, 1u);
+    }
+  }
+  __syncthreads();
+  const bool ok = *decision != 0;
+  __syncthreads();  // the decision word is rewritten by the next item's gate
+  if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
 // Persistent workgroup: runs the segments [ranges[2w], ranges[2w+1]) of the uploaded schedule.
-template <int D, bool FP8, bool OUT_F32>
+// GATED: every item first passes gate_item.
+template <int D, bool FP8, bool OUT_F32, bool GATED>
 __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
   using Loader = TileLoader<D, FP8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem_k[NBUF][BN * Loader::KB];
@@ -744,8 +783,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
   const int32_t* segs = p.blob + ld_const(hdr, H_OFF_SEGS);
   const int32_t* items = p.blob + ld_const(hdr, H_OFF_ITEMS);
   const int32_t* tiles = p.blob + ld_const(hdr, H_OFF_TILES);
+  __shared__ int gate_decision;
   for (int sg = s0; sg < s1; ++sg) {
-    run_segment<D, FP8, OUT_F32>(p, items, ld_const(segs, sg * kSegInts), ld_const(segs, sg * kSegInts + 1),
+    const int item = ld_const(segs, sg * kSegInts);
+    if constexpr (GATED) {
+      if (!gate_item(p, items, item, &gate_decision)) continue;
+    }
+    run_segment<D, FP8, OUT_F32, GATED>(p, items, item, ld_const(segs, sg * kSegInts + 1),
                                  ld_const(segs, sg * kSegInts + 2), ld_const(segs, sg * kSegInts + 3), tiles, smem_k, smem_v, redo_flags);
   }
 }
@@ -796,19 +840,21 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128) {
-    if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<128, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<128, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
+    if (p.gate_flags) hipLaunchKernelGGL((attn_fwd_kernel<128, false, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
+    else if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<128, false, true, false>), dim3(grid), dim3(NTHR), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<128, false, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
   } else {
-    if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<64, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<64, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
+    if (p.gate_flags) hipLaunchKernelGGL((attn_fwd_kernel<64, false, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
+    else if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<64, false, true, false>), dim3(grid), dim3(NTHR), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, false, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false>), dim3(grid), dim3(NTHR), 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_kernel<64, true, false>), dim3(grid), dim3(NTHR), 0, s, p);
+  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 

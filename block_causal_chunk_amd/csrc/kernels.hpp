@@ -24,11 +24,32 @@ struct FwdParams {
   float c;                 // softmax scale * log2(e)
   float scale;             // softmax scale
   uint32_t nonce_lo, nonce_hi;
+  // Optional gate: before a work item reads keys, every chunk it sees must have
+  // gate_flags[c] >= gate_need[c]; polled at most gate_spin times, else the item is skipped and
+  // bit 0 of *gate_status is set.  gate_flags == nullptr: no gate.
+  const uint32_t* gate_flags;
+  const uint32_t* gate_need;
+  uint32_t* gate_status;
+  int32_t gate_spin;
+};
+
+struct PublishParams {
+  const uint16_t* k_src;   // bf16 [tokens, H, D], projection layout
+  const uint16_t* v_src;
+  uint16_t* k_pool;        // bf16 [pool_rows, H, D]
+  uint16_t* v_pool;
+  const int32_t* blob;     // uploaded work list (device): chunk table and key tiles
+  int32_t chunk;
+  int32_t row_granules;    // 16-byte granules per token row (H * D * 2 / 16)
+  uint32_t nonce_lo, nonce_hi;
+  uint32_t* flags;         // nullptr, or flags[chunk] = generation after the copy
+  uint32_t generation;
 };
 
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s);
 hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, int head_dim, bool out_f32, int groups, hipStream_t s);
+hipError_t launch_publish(const PublishParams& p, int64_t tokens, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int32_t heads, int32_t head_dim,
                                uint8_t* x8, float* scales, hipStream_t s);

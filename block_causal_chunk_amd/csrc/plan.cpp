@@ -144,9 +144,11 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
     std::stable_sort(by_order.begin(), by_order.end(),
                      [&](int x, int y) { return table->chunk_order[x] < table->chunk_order[y]; });
     std::vector<int32_t> tiles;
-    std::vector<int32_t> prefix_end(n, 0);
+    std::vector<int32_t> prefix_end(n, 0), first_tile(n, 0), rank(n, 0), last_rank(n, 0);
     for (int r = 0; r < n; ++r) {
       const int c = by_order[r];
+      first_tile[c] = static_cast<int32_t>(tiles.size() / kTileInts);
+      rank[c] = last_rank[c] = r;
       const int32_t tok = table->chunk_tokens[c];
       for (int32_t p = table->page_offsets[c]; p < table->page_offsets[c + 1]; ++p) {
         const int32_t first_tok = (p - table->page_offsets[c]) * table->page_size;
@@ -160,8 +162,10 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
       prefix_end[c] = static_cast<int32_t>(tiles.size() / kTileInts);
     }
     for (int r = n - 2; r >= 0; --r)  // a tie group ends where its last member ends
-      if (table->chunk_order[by_order[r]] == table->chunk_order[by_order[r + 1]])
+      if (table->chunk_order[by_order[r]] == table->chunk_order[by_order[r + 1]]) {
         prefix_end[by_order[r]] = prefix_end[by_order[r + 1]];
+        last_rank[by_order[r]] = last_rank[by_order[r + 1]];
+      }
     P.n_tiles = static_cast<int32_t>(tiles.size() / kTileInts);
 
     // Items: (query chunk, query tile of up to kBlockM rows, head) with the whole visible prefix.
@@ -307,13 +311,15 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
     P.n_segs = static_cast<int32_t>(seg_ints.size() / kSegInts);
     P.n_wgs = static_cast<int32_t>(per_wg.size());
 
-    // Blob: header, items, segments, ranges, tiles, groups.
+    // Blob: header, items, segments, ranges, tiles, groups, chunks, chunk ids by rank.
     P.off_items = kHeaderInts;
     P.off_segs = P.off_items + static_cast<size_t>(n_items) * kItemInts;
     P.off_ranges = P.off_segs + seg_ints.size();
     P.off_tiles = P.off_ranges + ranges.size();
     P.off_groups = P.off_tiles + tiles.size();
-    P.blob.assign(P.off_groups + groups.size(), 0);
+    P.off_chunks = P.off_groups + groups.size();
+    P.off_byrank = P.off_chunks + static_cast<size_t>(n) * kChunkInts;
+    P.blob.assign(P.off_byrank + n, 0);
     int32_t* B = P.blob.data();
     B[H_MAGIC] = static_cast<int32_t>(kMagic);
     B[H_NONCE_LO] = static_cast<int32_t>(P.nonce & 0xffffffffu);
@@ -328,10 +334,19 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
     B[H_OFF_SEGS] = static_cast<int32_t>(P.off_segs);
     B[H_WGS] = P.n_wgs;
     B[H_OFF_RANGES] = static_cast<int32_t>(P.off_ranges);
+    B[H_CHUNKS] = n;
+    B[H_OFF_CHUNKS] = static_cast<int32_t>(P.off_chunks);
+    B[H_OFF_BYRANK] = static_cast<int32_t>(P.off_byrank);
     for (int i = 0; i < n_items; ++i) {
       const Item& it = items[i];
       int32_t* d = B + P.off_items + static_cast<size_t>(i) * kItemInts;
       d[0] = it.head; d[1] = it.q_row0; d[2] = it.rows; d[3] = it.qsb; d[4] = it.qchunk; d[5] = it.n_tiles;
+      d[6] = last_rank[table->query_chunks[it.qchunk]];  // chunks of rank 0..d[6] are visible
+    }
+    for (int c = 0; c < n; ++c) {
+      int32_t* d = B + P.off_chunks + static_cast<size_t>(c) * kChunkInts;
+      d[0] = first_tile[c]; d[1] = table->chunk_tokens[c]; d[2] = rank[c]; d[3] = last_rank[c];
+      B[P.off_byrank + rank[c]] = c;
     }
     std::copy(seg_ints.begin(), seg_ints.end(), B + P.off_segs);
     std::copy(ranges.begin(), ranges.end(), B + P.off_ranges);
@@ -423,6 +438,10 @@ extern "C" wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t
     case 5:
       src = P->blob.data() + P->off_ranges;
       total = static_cast<size_t>(P->n_wgs) * kRangeInts;
+      break;
+    case 6:
+      src = P->blob.data() + P->off_chunks;
+      total = static_cast<size_t>(P->num_chunks) * kChunkInts;
       break;
     default:
       return WFATTN_ERR_INVALID;

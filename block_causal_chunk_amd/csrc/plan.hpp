@@ -18,6 +18,7 @@ constexpr int kSegInts = 4;    // ints per segment
 constexpr int kRangeInts = 2;  // ints per workgroup range
 constexpr int kTileInts = 2;   // ints per key tile
 constexpr int kGroupInts = 4;  // ints per merge group
+constexpr int kChunkInts = 4;  // ints per chunk: first key tile, tokens, rank, last rank it sees
 constexpr int kHeaderInts = 16;
 constexpr uint32_t kMagic = 0x57464132u;  // "WFA2"
 
@@ -36,6 +37,9 @@ enum HeaderWord {
   H_OFF_SEGS = 10,
   H_WGS = 11,
   H_OFF_RANGES = 12,
+  H_CHUNKS = 13,
+  H_OFF_CHUNKS = 14,
+  H_OFF_BYRANK = 15,
 };
 
 struct Plan {
@@ -53,6 +57,7 @@ struct Plan {
   int32_t n_items = 0, n_tiles = 0, n_groups = 0, n_partials = 0, n_segs = 0, n_wgs = 0;
   std::vector<int32_t> blob;  // header, items, segments, ranges, key tiles, merge groups
   size_t off_items = 0, off_segs = 0, off_ranges = 0, off_tiles = 0, off_groups = 0;  // int32 offsets
+  size_t off_chunks = 0, off_byrank = 0;
   // workspace layout (bytes)
   size_t ws_blob = 0, ws_part_o = 0, ws_part_lse = 0, ws_stage = 0;
   size_t ws_base_bytes = 0;   // blob + partials

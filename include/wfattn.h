@@ -144,12 +144,14 @@ wfattn_status wfattn_plan_upload(const wfattn_plan_t* plan, void* ws, size_t ws_
  * what = 0: summary, 10 int32 (items, key tiles, merge groups, partial slots, block_m, block_n,
  *           most segments of one item, query chunks, segments, workgroups);
  * what = 1: items, 8 int32 each (head, first Q row, rows, first Q-scale block, query chunk
- *           index, visible key tiles, 0, 0);
+ *           index, visible key tiles, last visible chunk rank, 0);
  * what = 2: key tiles in clean -> noisy order, 2 int32 each (first pool row, valid keys);
  * what = 3: merge groups, 4 int32 each (item, first partial slot, parts, 0);
  * what = 4: segments in workgroup order, 4 int32 each (item, first key tile, end key tile,
  *           partial slot or -1);
- * what = 5: workgroups, 2 int32 each (first segment, end segment).
+ * what = 5: workgroups, 2 int32 each (first segment, end segment);
+ * what = 6: chunks by chunk id, 4 int32 each (first key tile, tokens, rank in clean -> noisy
+ *           order, last rank visible to it).
  * Copies min(cap, total) int32 into buf (buf may be NULL when cap == 0) and stores the total
  * count of int32 in *n.  Errors: NULL, INVALID (bad plan or unknown `what`). */
 wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t what, int32_t* buf,
@@ -185,6 +187,44 @@ wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const
  * (rows < 0 or heads < 1), DEVICE. */
 wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads,
                                   int32_t head_dim, uint8_t* x8, float* scales, void* stream);
+
+/* ---- producer side: publish a chunk's K/V, and a forward gated on it ------------------------
+ * The producers write each chunk's keys and values straight into the slots the consumer reads
+ * (project page, "03 - End-to-end KV transport", panel "03 - Layout"), and a consumer uses a
+ * chunk's states only once they are complete (KipQuest page, "The deep dive").  Ordering between
+ * a producer stream and the consumer's stream is the caller's (an event); the flags let the
+ * forward check, chunk by chunk, that what it is about to read is the generation it expects. */
+
+/* Write chunk `chunk`'s K and V, each bf16 [chunk_tokens[chunk], H, d] in projection layout
+ * (token-major, 16-byte aligned), into that chunk's pages of k_pool / v_pool (bf16
+ * [num_pages, page_size, H, d]): token u goes to page page_ids[page_offsets[chunk] + u/page_size],
+ * slot u % page_size.  Slots past the chunk's last token are not written.  If flags is not NULL
+ * (uint32 [num_chunks], device), flags[chunk] = generation is stored afterwards, on the same
+ * stream, with release ordering.  ws: a workspace filled by wfattn_plan_upload from this plan
+ * (it holds the page layout).  The chunk's pages may not be read by other work until this has run.
+ * Errors: NULL, INVALID (bad plan, chunk out of range), UNSUPPORTED (alignment), WORKSPACE,
+ * DEVICE. */
+wfattn_status wfattn_publish_kv(const wfattn_plan_t* plan, int32_t chunk, const void* k_src,
+                                const void* v_src, void* k_pool, void* v_pool, uint32_t* flags,
+                                uint32_t generation, const void* ws, size_t ws_bytes, void* stream);
+
+/* Upper bound of spin_limit in wfattn_fwd_gated: one poll is followed by a sleep of about 4000
+ * clocks, so a gate gives up after about 2 s at most. */
+#define WFATTN_GATE_SPIN_MAX (1 << 20)
+
+/* wfattn_fwd (bf16 I/O) with a gate: before a work item reads any key, every chunk b it sees must
+ * have flags[b] >= need[b] (uint32 device arrays [num_chunks]).  The item's first wave polls the
+ * flags with acquire loads at most spin_limit + 1 times (0: check once, never wait), sleeping
+ * between polls; if they are still short, the item is skipped and bit 0 of *gate_status (device,
+ * set with an atomic OR, never cleared by the library) is set.  Rows of skipped items, and of
+ * items merged with them, are then unspecified; every other row is exact.  A wait never
+ * deadlocks: it ends after spin_limit polls even if no producer ever runs.
+ * Errors: as wfattn_fwd, plus NULL (flags, need, gate_status), RANGE (spin_limit < 0 or above
+ * WFATTN_GATE_SPIN_MAX). */
+wfattn_status wfattn_fwd_gated(const wfattn_plan_t* plan, const void* q, const void* k_pool,
+                               const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes,
+                               const uint32_t* flags, const uint32_t* need, int32_t spin_limit,
+                               uint32_t* gate_status, void* stream);
 
 /* Static string naming a status. */
 const char* wfattn_status_str(wfattn_status status);

@@ -6,7 +6,8 @@ import this package.  The product path (the HIP library and its binding) never d
 Two independent statements of the same definition live here:
   * ``wf_oracle.c`` (fp64, OpenMP): walks the page table chunk by chunk, two-pass softmax;
   * ``dense.py`` (numpy fp64): gathers keys, builds an explicit block-lower-triangular mask.
-plus an e4m3 codec and block quantizer written from the OCP 8-bit float definition.
+plus an e4m3 codec and block quantizer written from the OCP 8-bit float definition, and the
+placement of a chunk's K/V into its pages (``publish_kv``).
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py``.
 """
 from __future__ import annotations
@@ -118,6 +119,22 @@ def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
     if rc != 0:
         raise ValueError("oracle_attn_rows failed with code %d" % rc)
     return out, lse
+
+
+def publish_kv(table, chunk: int, k_src, v_src, k_pool, v_pool):
+    """Place chunk ``chunk``'s keys and values, [tokens, H, d] in token order, into its pages:
+    token u goes to physical page page_ids[page_offsets[chunk] + u // page_size], slot
+    u % page_size (the producer writes into the consumer's fixed slots: Wave Forcing project
+    page, "03 - End-to-end KV transport", panel "03 - Layout").  Returns new pools (numpy, the
+    inputs' dtype); every other slot keeps its value."""
+    kp, vp = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    ks, vs = np.asarray(k_src), np.asarray(v_src)
+    first = int(table.page_offsets[chunk])
+    for u in range(int(table.chunk_tokens[chunk])):
+        page = int(table.page_ids[first + u // int(table.page_size)])
+        kp[page, u % int(table.page_size)] = ks[u]
+        vp[page, u % int(table.page_size)] = vs[u]
+    return kp, vp
 
 
 def attn_masked(q, k, v, allowed, scale: float, nthreads: int = 0):

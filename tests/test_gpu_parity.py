@@ -172,6 +172,112 @@ def test_store_rank_query_shape(B, O):
     assert np.abs(f64(lse).T[rows] - ref_lse).max() <= LSE_TOL
 
 
+# ------------------------------------------------------------------ publish + gate
+def _chunk_rows(c, b):
+    """Chunk b's K and V rows in token order, read out of the case's pool by the oracle's gather."""
+    from oracle.dense import gather_keys
+    k16 = c.k_pool.view(torch.int16).numpy()
+    v16 = c.v_pool.view(torch.int16).numpy()
+    gk, owner = gather_keys(c.table, k16.astype(np.float64))
+    gv, _ = gather_keys(c.table, v16.astype(np.float64))
+    to = lambda x: torch.from_numpy(x[owner == b].astype(np.int16)).view(torch.bfloat16)
+    return to(gk), to(gv)
+
+
+def test_publish_bit_exact(B, O):
+    """Every token of a chunk lands in its slot bit for bit as the oracle places it; no other slot
+    (other chunks, padding) changes; the flag carries the generation."""
+    rng = np.random.default_rng(51)
+    t = make_table([300, 129, 64, 700, 1], [2, 0, 1, 3, 4], [3], 256, 3, 128, shuffle_rng=rng, spare=2)
+    c = fill_case("pub", t, rng, torch.bfloat16)
+    att = B.Attention(t)
+    kp, vp = c.k_pool.clone().cuda(), c.v_pool.clone().cuda()
+    ref_k, ref_v = c.k_pool.view(torch.int16).numpy(), c.v_pool.view(torch.int16).numpy()
+    flags = torch.zeros(t.num_chunks, dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(3)
+    for b in range(t.num_chunks):
+        n = int(t.chunk_tokens[b])
+        sk = torch.randn(n, 3, 128, generator=g).to(torch.bfloat16)
+        sv = torch.randn(n, 3, 128, generator=g).to(torch.bfloat16)
+        print(f"[case] publish chunk {b} ({n} tokens)", flush=True)
+        B.wfattn_publish_kv(att.plan, b, sk.cuda(), sv.cuda(), kp, vp, flags, 40 + b, att.ws)
+        ref_k, ref_v = O.publish_kv(t, b, sk.view(torch.int16).numpy(), sv.view(torch.int16).numpy(), ref_k, ref_v)
+    torch.cuda.synchronize()
+    assert (kp.cpu().view(torch.int16).numpy() == ref_k).all()
+    assert (vp.cpu().view(torch.int16).numpy() == ref_v).all()
+    assert flags.cpu().tolist() == [40 + b for b in range(t.num_chunks)]
+
+
+def test_publish_then_gated_forward_on_two_streams(B, O):
+    """A producer stream publishes the query chunk's own K/V (the last state to be produced) into a
+    pool where its pages are still NaN and raises its flag; the consumer stream waits on an event
+    and runs the gated forward.  Output and LSE match the oracle; the gate reports nothing."""
+    c = medium_case("wan13b_task", seed=9)
+    t = c.table
+    sk, sv = _chunk_rows(c, 3)
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    _poison_chunks(c, [3])  # the pool as the consumer finds it before the publish
+    kp_dev, vp_dev = c.k_pool.cuda(), c.v_pool.cuda()
+    c.k_pool, c.v_pool = kp, vp  # the oracle sees the published values
+    att = B.Attention(t)
+    flags = torch.tensor([5, 5, 5, 0], dtype=torch.int32, device="cuda")  # chunks 0-2 published earlier
+    need = torch.full((4,), 5, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((t.lq, t.num_heads, t.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((t.num_heads, t.lq), dtype=torch.float32, device="cuda")
+    q = c.q.cuda()
+    torch.cuda.synchronize()
+    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    print("[case] publish on a producer stream, gated forward on a consumer stream", flush=True)
+    with torch.cuda.stream(producer):
+        B.wfattn_publish_kv(att.plan, 3, sk.cuda(), sv.cuda(), kp_dev, vp_dev, flags, 5, att.ws, stream=producer)
+        ev = torch.cuda.Event()
+        ev.record(producer)
+    consumer.wait_event(ev)
+    B.wfattn_fwd_gated(att.plan, q, kp_dev, vp_dev, out, lse, att.ws, flags, need, 1000, status, stream=consumer)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+    check_bf16(f64(out), ref, "gated")
+    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+
+
+def test_gate_skips_items_of_unpublished_chunks(B, O):
+    """Query chunks with different prefixes; the noisiest chunk's flag is short.  Its items are
+    skipped after a bounded poll (their rows keep the caller's sentinel), bit 0 of the status is
+    set, and every other query chunk's rows are exact.  Once the flag is raised, the same call
+    reports nothing and matches the oracle everywhere."""
+    c = medium_case("wave_round", seed=13)  # query chunks 2..6 of 7
+    t = c.table
+    q, k, v = to_dev(c)
+    att = B.Attention(t, split_k=1)
+    n = t.num_chunks
+    need = torch.full((n,), 2, dtype=torch.int32, device="cuda")
+    flags = torch.full((n,), 2, dtype=torch.int32, device="cuda")
+    flags[6] = 1  # chunk 6 (the noisiest, a query chunk itself) is one generation behind
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((t.lq, t.num_heads, t.head_dim), 7.0, dtype=torch.bfloat16, device="cuda")
+    print("[case] gate with chunk 6 unpublished, spin_limit 3", flush=True)
+    B.wfattn_fwd_gated(att.plan, q, k, v, out, None, att.ws, flags, need, 3, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    ref, _ = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+    qstart = np.concatenate([[0], np.cumsum([int(t.chunk_tokens[a]) for a in t.query_chunks])])
+    last = list(t.query_chunks).index(6)
+    r0, r1 = qstart[last], qstart[last + 1]
+    got = f64(out)
+    assert (got[r0:r1] == 7.0).all()
+    keep = np.r_[0:r0, r1:t.lq]
+    check_bf16(got[keep], ref[keep], "gate-partial")
+    flags[6] = 2
+    status.zero_()
+    print("[case] gate with every chunk published", flush=True)
+    B.wfattn_fwd_gated(att.plan, q, k, v, out, None, att.ws, flags, need, 0, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check_bf16(f64(out), ref, "gate-open")
+
+
 # ------------------------------------------------------------------ invariants (bitwise)
 def test_page_shuffle_is_bitwise_identical(B):
     c = medium_case("long_rollout", seed=5)

@@ -4,7 +4,8 @@ P1 dense explicit mask, P2 a library routine (torch SDPA in float64), P3 the sin
 case, P4 closed forms, P5 permutation/page-shuffle invariance, P6 no reverse edge, P7
 decomposition of a multi-chunk query set, P8 the e4m3 codec against the OCP definition and
 torch's float8_e4m3fn, P9 merging key partitions through their LSEs, P10 ties in chunk order (full
-attention when all tie, a tie group equals one merged chunk, SDPA), plus brute force on tiny
+attention when all tie, a tie group equals one merged chunk, SDPA), P11 placing a chunk's K/V
+into its pages (round trip through the dense gather, rebuilding the input pool), plus brute force on tiny
 inputs, a hand-derived closed-form fixture, and checks that plausible mistakes would be caught.
 """
 import json
@@ -147,6 +148,45 @@ def test_p10_ties_sdpa_and_dense(oracle_lib, seed):
     k2, k4, k5 = sum(tokens[:2]), sum(tokens[:4]), sum(tokens[:5])
     assert m[0, k2:k2 + tokens[2]].all() and m[tokens[4], k4:k4 + tokens[4]].all()
     assert not m[0, k5:].any() and not m[tokens[4], k5:].any()
+
+
+# ---------------------------------------------------------------- P11: publishing K/V into pages
+def test_p11_publish_round_trips_through_the_dense_gather(oracle_lib):
+    """Publishing a chunk then reading the pool back with the dense form's gather gives the
+    source rows; slots of other chunks and padding slots keep their values."""
+    from oracle.dense import gather_keys
+    rng = np.random.default_rng(21)
+    t = make_table([70, 129, 64, 5], [1, 0, 3, 2], [0], 64, 2, 16, shuffle_rng=rng, spare=3)
+    kp = rng.standard_normal((t.num_pages, t.page_size, 2, 16))
+    vp = rng.standard_normal(kp.shape)
+    c = 1
+    ks = rng.standard_normal((int(t.chunk_tokens[c]), 2, 16))
+    vs = rng.standard_normal(ks.shape)
+    k2, v2 = oracle_lib.publish_kv(t, c, ks, vs, kp, vp)
+    gk, owner = gather_keys(t, k2)
+    gv, _ = gather_keys(t, v2)
+    assert (gk[owner == c] == ks).all() and (gv[owner == c] == vs).all()
+    gk0, _ = gather_keys(t, kp)
+    assert (gk[owner != c] == gk0[owner != c]).all()
+    changed = set((int(p), int(q)) for p, q in np.argwhere((k2 != kp).any(axis=(2, 3))))
+    first = int(t.page_offsets[c])
+    expect = set((int(t.page_ids[first + u // t.page_size]), u % t.page_size) for u in range(int(t.chunk_tokens[c])))
+    assert changed == expect  # exactly the chunk's token slots
+
+
+def test_p11_publishing_every_chunk_rebuilds_the_input_pool(oracle_lib):
+    """The inputs module lays a case's draws into its pool independently; publishing each chunk's
+    rows (read back by the dense gather) into an all-NaN pool rebuilds it exactly, padding too."""
+    from oracle.dense import gather_keys
+    c = make_case("wave_round", small=True)
+    gk, owner = gather_keys(c.table, c.k_pool)
+    gv, _ = gather_keys(c.table, c.v_pool)
+    kp = np.full(c.k_pool.shape, np.nan)
+    vp = np.full(c.v_pool.shape, np.nan)
+    for b in range(c.table.num_chunks):
+        kp, vp = oracle_lib.publish_kv(c.table, b, gk[owner == b], gv[owner == b], kp, vp)
+    same = lambda a, b: ((a == b) | (np.isnan(a) & np.isnan(b))).all()
+    assert same(kp, c.k_pool.double().numpy()) and same(vp, c.v_pool.double().numpy())
 
 
 # ---------------------------------------------------------------- P3: single chunk

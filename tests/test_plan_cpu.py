@@ -133,6 +133,27 @@ def test_call_errors_before_any_hip_call(B):
     assert L.wfattn_quantize_fp8(A, 10, 2, 96, A, A, None) == B.WFATTN_ERR_UNSUPPORTED
     assert L.wfattn_quantize_fp8(A, -1, 2, 128, A, A, None) == B.WFATTN_ERR_RANGE
     assert L.wfattn_quantize_fp8(A, 10, 0, 128, A, A, None) == B.WFATTN_ERR_RANGE
+    # publishing a chunk's K/V
+    P = L.wfattn_publish_kv
+    assert P(None, 1, A, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert P(h, 1, None, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert P(h, 1, A, A, A, None, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert P(ctypes.addressof(bogus), 1, A, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID
+    assert P(h, 3, A, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID  # 3 chunks: ids 0..2
+    assert P(h, -1, A, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID
+    assert P(h, 1, A + 8, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert P(h, 1, A, A, A, A, A + 2, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert P(h, 1, A, A, A, A, A, 3, None, ws_need, None) == B.WFATTN_ERR_WORKSPACE
+    assert P(h, 1, A, A, A, A, A, 3, A, ws_need - 1, None) == B.WFATTN_ERR_WORKSPACE
+    # the gated forward
+    G = L.wfattn_fwd_gated
+    assert G(h, A, A, A, A, None, A, ws_need, None, A, 0, A, None) == B.WFATTN_ERR_NULL
+    assert G(h, A, A, A, A, None, A, ws_need, A, A, 0, None, None) == B.WFATTN_ERR_NULL
+    assert G(h, A, A, A, A, None, A, ws_need, A, A, -1, A, None) == B.WFATTN_ERR_RANGE
+    assert G(h, A, A, A, A, None, A, ws_need, A, A, B.WFATTN_GATE_SPIN_MAX + 1, A, None) == B.WFATTN_ERR_RANGE
+    assert G(h, A, A, A, A, None, A, ws_need, A + 2, A, 0, A, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert G(h, None, A, A, A, None, A, ws_need, A, A, 0, A, None) == B.WFATTN_ERR_NULL
+    assert G(h, A, A, A, A, None, A, ws_need - 1, A, A, 0, A, None) == B.WFATTN_ERR_WORKSPACE
     assert L.wfattn_quantize_fp8(A + 8, 10, 2, 128, A, A, None) == B.WFATTN_ERR_UNSUPPORTED
     assert L.wfattn_quantize_fp8(A, 0, 2, 128, A, A, None) == B.WFATTN_OK  # nothing to do, no launch
     assert L.wfattn_query_rows(None) == -1
