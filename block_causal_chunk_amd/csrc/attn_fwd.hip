@@ -736,20 +736,27 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
 }
 
 // Gate of one work item: every chunk of rank 0 .. last (the item's visible chunks) must carry a
-// generation flag at least the one the caller needs.  Wave 0 polls with acquire loads (at most
-// gate_spin sleeps, so the wait always ends) and the decision is shared through LDS, so the whole
-// workgroup takes the same branch.  A chunk that is not ready skips the item and sets bit 0 of
-// the caller's status word.
+// generation flag at least the one the caller needs.  Wave 0 polls (at most gate_spin sleeps, so
+// the wait always ends) and the decision is shared through LDS, so the whole workgroup takes the
+// same branch.  A chunk that is not ready skips the item and sets bit 0 of the caller's status.
+//
+// Memory ordering.  The flags are read with device-coherent (agent-scope) atomic loads.  No key or
+// value of a chunk is read in this kernel before its flag is seen (every item of every workgroup
+// passes this gate first), and the caches hold nothing of this kernel's from before its start, so
+// a chunk's pages cannot be stale in any cache once its flag is up.  An agent-scope acquire would
+// invalidate this XCD's L2 at every item and throw away the K/V reuse between the workgroups that
+// share it; it is issued only after a poll that had to wait for a producer running alongside.
 __device__ bool gate_item(const FwdParams& p, const int32_t* items, int item, int* decision) {
   const int32_t* byrank = p.blob + ld_const(p.blob, H_OFF_BYRANK);
   const int last = ld_const(items, item * kItemInts + 6);
   if (threadIdx.x < 64) {
     bool ready = false;
-    for (int it = 0;; ++it) {
+    int it = 0;
+    for (;; ++it) {
       bool mine = true;
       for (int r = threadIdx.x; r <= last; r += 64) {
         const int c = byrank[r];
-        const uint32_t f = __hip_atomic_load(p.gate_flags + c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t f = __hip_atomic_load(p.gate_flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         mine = mine && f >= p.gate_need[c];
       }
       ready = __all(mine);
@@ -757,15 +764,15 @@ __device__ bool gate_item(const FwdParams& p, const int32_t* items, int item, in
       __builtin_amdgcn_s_sleep(63);
     }
     if (threadIdx.x == 0) {
-      *decision = ready ? 1 : 0;
+      *decision = !ready ? 0 : (it == 0 ? 1 : 2);
       if (!ready) atomicOr(p.gate_status, 1u);
     }
   }
   __syncthreads();
-  const bool ok = *decision != 0;
+  const int dec = *decision;
   __syncthreads();  // the decision word is rewritten by the next item's gate
-  if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
+  if (dec == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return dec != 0;
 }
 
 // Persistent workgroup: runs the segments [ranges[2w], ranges[2w+1]) of the uploaded schedule.
