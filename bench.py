@@ -96,6 +96,33 @@ def mfma_counters_from_profiles(workload: str):
     return {k: d[k] for k in ("mfma_busy_frac", "valu_coexec_frac_of_mfma_busy", "active_clock_ghz")}
 
 
+def publish_fp8(B, att, t, q, k8, ks, v, reps: int = 20):
+    """Outside the timed steps: wfattn_publish_kv_fp8 of the query chunk (K quantized to e4m3 per
+    64-token block and head into the K8 pool, V copied), HBM-bound: 2 B read + 1 B written per K
+    element, 2 + 2 B per V element, plus the scales."""
+    import torch
+    H, d = t.num_heads, t.head_dim
+    a = int(t.query_chunks[0])
+    n = int(t.chunk_tokens[a])
+    sk = torch.randn((n, H, d), device=q.device).to(torch.bfloat16)
+    sv = torch.randn((n, H, d), device=q.device).to(torch.bfloat16)
+    k8p, ksp, vp = k8.clone(), ks.clone(), v.clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        B.wfattn_publish_kv_fp8(att.plan, a, sk, sv, k8p, ksp, vp, None, 0, att.ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        B.wfattn_publish_kv_fp8(att.plan, a, sk, sv, k8p, ksp, vp, None, 0, att.ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = n * H * d * (2 + 1 + 2 + 2) + (-(-n // 64)) * H * 4
+    return {"publish_kv_fp8": {"chunk_tokens": n, "ms": round(ms, 4), "bytes": nbytes,
+                               "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(nbytes / (ms * 1e-3) / 8e12, 4)}}
+
+
 def publish_and_gate(B, att, t, q, k, v, reps: int = 20):
     """Outside the timed steps: (1) wfattn_publish_kv of the (first) query chunk's K/V from
     projection layout into its pages, an HBM-bound copy (read + write of K and V); (2) the gated
@@ -290,7 +317,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
-    extra = {} if fp8 or f32 else publish_and_gate(B, att, t, q, k, v)
+    extra = {} if f32 else (publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v))
     ms = float(per.mean())
     flops = effective_flops(t)
     tflops = flops / (ms * 1e-3) / 1e12

@@ -21,7 +21,7 @@ WFATTN_WS_BF16, WFATTN_WS_FP32, WFATTN_WS_FP8 = 0, 1, 2
 EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_workspace_bytes",
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
-            "wfattn_fwd_gated"]
+            "wfattn_fwd_gated", "wfattn_publish_kv_fp8"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 
 
@@ -79,6 +79,8 @@ def lib():
         L.wfattn_publish_kv.restype = i32
         L.wfattn_fwd_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, vp, vp]
         L.wfattn_fwd_gated.restype = i32
+        L.wfattn_publish_kv_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
+        L.wfattn_publish_kv_fp8.restype = i32
         L.wfattn_status_str.argtypes = [i32]
         L.wfattn_status_str.restype = ctypes.c_char_p
         L.wfattn_abi_version.argtypes = []
@@ -183,6 +185,14 @@ def wfattn_publish_kv(plan: Plan, chunk: int, k_src, v_src, k_pool, v_pool, flag
     _check(lib().wfattn_publish_kv(plan.handle, int(chunk), _ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
                                    _ptr(flags), int(generation) & 0xffffffff, _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "wfattn_publish_kv")
+
+
+def wfattn_publish_kv_fp8(plan: Plan, chunk: int, k_src, v_src, k8_pool, k_scale, v_pool, flags, generation: int,
+                          ws, stream=None):
+    _check(lib().wfattn_publish_kv_fp8(plan.handle, int(chunk), _ptr(k_src), _ptr(v_src), _ptr(k8_pool),
+                                       _ptr(k_scale), _ptr(v_pool), _ptr(flags), int(generation) & 0xffffffff,
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "wfattn_publish_kv_fp8")
 
 
 def wfattn_fwd_gated(plan: Plan, q, k_pool, v_pool, out, lse, ws, flags, need, spin_limit: int, gate_status,

@@ -167,6 +167,38 @@ extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t
   return WFATTN_OK;
 }
 
+extern "C" wfattn_status wfattn_publish_kv_fp8(const wfattn_plan_t* plan, int32_t chunk, const void* k_src,
+                                               const void* v_src, uint8_t* k8_pool, float* k_scale, void* v_pool,
+                                               uint32_t* flags, uint32_t generation, const void* ws, size_t ws_bytes,
+                                               void* stream) {
+  if (!plan || !k_src || !v_src || !k8_pool || !k_scale || !v_pool) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  const Plan* P = as_plan(plan);
+  if (chunk < 0 || chunk >= P->num_chunks) return WFATTN_ERR_INVALID;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k8_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(k_scale, 4) || !aligned(flags, 4) || !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  PublishFp8Params pp{};
+  pp.k_src = static_cast<const uint16_t*>(k_src);
+  pp.v_src = static_cast<const uint16_t*>(v_src);
+  pp.k8_pool = k8_pool;
+  pp.k_scale = k_scale;
+  pp.v_pool = static_cast<uint16_t*>(v_pool);
+  pp.blob = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + P->ws_blob);
+  pp.chunk = chunk;
+  pp.heads = P->num_heads;
+  pp.nonce_lo = static_cast<uint32_t>(P->nonce & 0xffffffffu);
+  pp.nonce_hi = static_cast<uint32_t>(P->nonce >> 32);
+  pp.flags = flags;
+  pp.generation = generation;
+  const int64_t tokens = P->blob[P->off_chunks + static_cast<size_t>(chunk) * kChunkInts + 1];
+  return launch_publish_fp8(pp, tokens, P->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? WFATTN_OK
+             : WFATTN_ERR_DEVICE;
+}
+
 extern "C" wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads, int32_t head_dim,
                                              uint8_t* x8, float* scales, void* stream) {
   if (!x_bf16 || !x8 || !scales) return WFATTN_ERR_NULL;

@@ -50,11 +50,12 @@ hipError_t launch_publish(const PublishParams& p, int64_t tokens, hipStream_t s)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.flags) {
-    hipLaunchKernelGGL(flag_kernel, dim3(1), dim3(1), 0, s, p.flags, p.chunk, p.generation);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return p.flags ? launch_flag(p.flags, p.chunk, p.generation, s) : hipSuccess;
+}
+
+hipError_t launch_flag(uint32_t* flags, int32_t chunk, uint32_t generation, hipStream_t s) {
+  hipLaunchKernelGGL(flag_kernel, dim3(1), dim3(1), 0, s, flags, chunk, generation);
+  return hipGetLastError();
 }
 
 }  // namespace wfattn

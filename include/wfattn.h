@@ -208,6 +208,17 @@ wfattn_status wfattn_publish_kv(const wfattn_plan_t* plan, int32_t chunk, const 
                                 const void* v_src, void* k_pool, void* v_pool, uint32_t* flags,
                                 uint32_t generation, const void* ws, size_t ws_bytes, void* stream);
 
+/* Publish for the e4m3 path: like wfattn_publish_kv, but K goes into k8_pool (e4m3 codes,
+ * [num_pages, page_size, H, d]) with its scales in k_scale ([num_pages * page_size / 64, H]),
+ * quantized exactly as wfattn_quantize_fp8 does, one block per 64 tokens of the chunk and head
+ * (each block is one page-aligned 64-row block of the pool).  Only the chunk's tokens enter a
+ * block's amax; pool slots past the chunk's end are not written.  V is copied as bf16.
+ * Errors as wfattn_publish_kv. */
+wfattn_status wfattn_publish_kv_fp8(const wfattn_plan_t* plan, int32_t chunk, const void* k_src,
+                                    const void* v_src, uint8_t* k8_pool, float* k_scale,
+                                    void* v_pool, uint32_t* flags, uint32_t generation,
+                                    const void* ws, size_t ws_bytes, void* stream);
+
 /* Upper bound of spin_limit in wfattn_fwd_gated: one poll is followed by a sleep of about 4000
  * clocks, so a gate gives up after about 2 s at most. */
 #define WFATTN_GATE_SPIN_MAX (1 << 20)

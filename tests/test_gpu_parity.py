@@ -456,6 +456,69 @@ def test_fp8_small_all_elements(B, O, name, split_k):
         check_fp8_contract(got, ref, name)
 
 
+def test_publish_fp8_bit_exact(B, O):
+    """e4m3 publish: per 64-token block of the chunk and head, the codes and the scale are the
+    oracle quantizer's, placed in the chunk's pool rows and page-aligned scale blocks; V is copied
+    bit for bit; nothing else in the pools changes."""
+    rng = np.random.default_rng(61)
+    H, d = 3, 128
+    t = make_table([300, 129, 64, 1, 200], [1, 0, 2, 3, 4], [4], 256, H, d, shuffle_rng=rng, spare=2)
+    att = B.Attention(t, mode=B.WFATTN_WS_FP8)
+    rows = t.num_pages * t.page_size
+    k8 = torch.full((rows, H, d), 0x55, dtype=torch.uint8, device="cuda")
+    ks = torch.full((rows // 64, H), -1.0, dtype=torch.float32, device="cuda")
+    vp = torch.full((t.num_pages, t.page_size, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ref8 = np.full((t.num_pages, t.page_size, H, d), 0x55, np.uint8)
+    refs = np.full((rows // 64, H), -1.0, np.float32)
+    refv = vp.cpu().view(torch.int16).numpy()
+    flags = torch.zeros(t.num_chunks, dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(5)
+    for b in range(t.num_chunks):
+        n = int(t.chunk_tokens[b])
+        sk = (torch.randn(n, H, d, generator=g) * (1 + b)).to(torch.bfloat16)
+        sk[min(3, n - 1), 1, 7] = float("nan")  # a NaN is kept and ignored by the block amax
+        sv = torch.randn(n, H, d, generator=g).to(torch.bfloat16)
+        print(f"[case] e4m3 publish chunk {b} ({n} tokens)", flush=True)
+        B.wfattn_publish_kv_fp8(att.plan, b, sk.cuda(), sv.cuda(), k8, ks, vp, flags, 9, att.ws)
+        c8, csc = O.quantize_e4m3(sk)
+        ref8, refv = O.publish_kv(t, b, c8, sv.view(torch.int16).numpy(), ref8, refv)
+        first = int(t.page_offsets[b])
+        for blk in range(csc.shape[0]):
+            u = 64 * blk
+            row0 = int(t.page_ids[first + u // t.page_size]) * t.page_size + u % t.page_size
+            refs[row0 // 64] = csc[blk]
+    torch.cuda.synchronize()
+    got8 = k8.cpu().numpy().reshape(ref8.shape)
+    nan = np.isnan(O.e4m3_decode(ref8).reshape(ref8.shape))
+    assert np.array_equal(got8[~nan], ref8[~nan]) and np.isin(got8[nan], [0x7F, 0xFF]).all()
+    assert np.array_equal(ks.cpu().numpy(), refs)
+    assert np.array_equal(vp.cpu().view(torch.int16).numpy(), refv)
+    assert flags.cpu().tolist() == [9] * t.num_chunks
+
+
+def test_publish_fp8_feeds_the_fp8_forward(B, O):
+    """Pools built chunk by chunk with the e4m3 publish give the e4m3 forward bit for bit the
+    result of quantizing the whole (NaN-padded) pool at once: NaN padding never enters a block's
+    amax, so the two agree on every scale and code."""
+    c = make_case("wan14b_fp8", small=True)
+    t = c.table
+    H, d = t.num_heads, t.head_dim
+    out_ref, _ = run_fp8(B, c)
+    att = B.Attention(t, mode=B.WFATTN_WS_FP8)
+    rows = t.num_pages * t.page_size
+    k8 = torch.zeros((rows, H, d), dtype=torch.uint8, device="cuda")
+    ks = torch.ones((rows // 64, H), dtype=torch.float32, device="cuda")
+    vp = torch.full(c.v_pool.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b in range(t.num_chunks):
+        sk, sv = _chunk_rows(c, b)
+        B.wfattn_publish_kv_fp8(att.plan, b, sk.cuda(), sv.cuda(), k8, ks, vp, None, 0, att.ws)
+    q8, qs = B.quantize_q_fp8(t, c.q.cuda())
+    print("[case] e4m3 forward over published pools", flush=True)
+    out, _ = att.fwd_fp8(q8, qs, k8.view(c.k_pool.shape), ks, vp)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), out_ref.cpu().view(torch.int16))
+
+
 def test_fp8_full_size_sampled_rows(B, O):
     c = make_case("wan14b_fp8")
     print("[case] fp8 full wan14b_fp8", flush=True)

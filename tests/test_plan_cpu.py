@@ -145,6 +145,13 @@ def test_call_errors_before_any_hip_call(B):
     assert P(h, 1, A, A, A, A, A + 2, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
     assert P(h, 1, A, A, A, A, A, 3, None, ws_need, None) == B.WFATTN_ERR_WORKSPACE
     assert P(h, 1, A, A, A, A, A, 3, A, ws_need - 1, None) == B.WFATTN_ERR_WORKSPACE
+    P8 = L.wfattn_publish_kv_fp8
+    assert P8(h, 1, A, A, None, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert P8(h, 1, A, A, A, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert P8(h, 7, A, A, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID
+    assert P8(h, 1, A, A, A, A + 2, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert P8(h, 1, A, A, A + 8, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert P8(h, 1, A, A, A, A, A, A, 3, None, ws_need, None) == B.WFATTN_ERR_WORKSPACE
     # the gated forward
     G = L.wfattn_fwd_gated
     assert G(h, A, A, A, A, None, A, ws_need, None, A, 0, A, None) == B.WFATTN_ERR_NULL
