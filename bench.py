@@ -4,7 +4,7 @@ One step = one wfattn_fwd call (every kernel of the hot path) over one DiT layer
 one chunk-stage task, with inputs resident in HBM; the plan and its upload are built once per
 round and timed separately.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--no-cpu-baseline] [--no-extras]
 
 Default workload: the Wan-1.3B chunk task (H=12, d=128, 4680 query tokens of one chunk against
 18720 keys of the own chunk and three earlier ones, 256-token shuffled pages), bf16.
@@ -93,7 +93,9 @@ def mfma_counters_from_profiles(workload: str):
         return None
     if d.get("kernel_src_sha") != kernel_src_hash():
         return None
-    return {k: d[k] for k in ("mfma_busy_frac", "valu_coexec_frac_of_mfma_busy", "active_clock_ghz")}
+    keys = ("mfma_busy_frac", "valu_coexec_frac_of_mfma_busy", "active_clock_ghz", "l2_hit_rate",
+            "lds_bank_conflict_ratio")
+    return {k: d[k] for k in keys if k in d}
 
 
 def publish_fp8(B, att, t, q, k8, ks, v, reps: int = 20):
@@ -222,7 +224,20 @@ def cpu_baseline(case, budget_s: float = 12.0):
     flops = sum(4.0 * t.head_dim * t.num_heads * vis[int(np.searchsorted(qstart, r, side="right") - 1)] for r in rows)
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.max_threads(), kind="oracle",
                 sample=f"{len(rows)} of {lq} query rows (all {t.num_heads} heads), fp64, {dt:.1f} s",
-                seconds=dt)
+                seconds=dt, cpu=cpu_model())
+
+
+def cpu_model() -> str:
+    """Model name of the host CPU and the logical CPUs this process may use."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{name}, {len(os.sched_getaffinity(0))} logical CPUs available"
 
 
 def main():
@@ -235,6 +250,8 @@ def main():
     ap.add_argument("--xcd-remap", type=int, default=0)
     ap.add_argument("--cold", action="store_true", help="evict the 256 MB Infinity Cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the publish and gated-forward measurements (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (3 times) so that a "
@@ -317,13 +334,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
-    extra = {} if f32 else (publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v))
+    extra = {}
+    if not (f32 or args.no_extras):
+        extra = publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v)
     ms = float(per.mean())
     flops = effective_flops(t)
     tflops = flops / (ms * 1e-3) / 1e12
-    tasks = len(t.query_chunks) / (ms * 1e-3)
+    tasks = len(t.query_chunks) / (float(np.median(per)) * 1e-3)  # per the p50 call
     peak = PEAK_MIXED if fp8 else PEAK_BF16
     staged, unique = gather_bytes(t, 1 if fp8 else 2)
+    exps = flops / (4.0 * d)  # one exponential per unmasked (query row, key, head)
+    counters = mfma_counters_from_profiles(args.workload)
+    if counters is not None:
+        # the roofline peak again at the clock the kernel actually ran at under load
+        counters["peak_at_active_clock"] = round(peak * counters["active_clock_ghz"] / 2.4, 1)
+        counters["frac_at_active_clock"] = round(tflops / counters["peak_at_active_clock"], 4)
     traffic = traffic_from_profiles(args.workload)
     sec = ms * 1e-3
     gather = {"lds_staged_bytes": staged, "lds_staged_gbs": round(staged / sec / 1e9, 1),
@@ -356,7 +381,8 @@ def main():
                  "splits": int(summary[6]), "block_m": int(summary[4]), "block_n": int(summary[5])},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic},
-        "mfma_counters": mfma_counters_from_profiles(args.workload),
+        "mfma_counters": counters,
+        "exps_per_s": round(exps / (ms * 1e-3), 1),
         "gather": gather,
         "wall_s_timed": round(wall, 3),
     }
@@ -367,6 +393,7 @@ def main():
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
         res["cpu_baseline"]["value"] = round(res["cpu_baseline"]["value"], 6)
         res["cpu_baseline"]["seconds"] = round(res["cpu_baseline"]["seconds"], 2)
+        res["cpu_baseline"]["gpu_over_cpu"] = round(tflops / res["cpu_baseline"]["value"], 1)
     print(json.dumps(res), flush=True)
 
 
