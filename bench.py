@@ -98,6 +98,47 @@ def mfma_counters_from_profiles(workload: str):
     return {k: d[k] for k in keys if k in d}
 
 
+def rope_publish(B, att, t, k_pool, k8_pool, k_scale, v, reps: int = 20):
+    """Outside the timed steps: the fused pre-attention epilogue of the (first) query chunk, from a
+    [tokens, 3, H, d] projection output: rotate Q and K, write Q (bf16, or e4m3 with block scales
+    when k8_pool is given) and publish K (bf16 or e4m3) and V into the pages.  HBM-bound."""
+    import torch
+    H, d = t.num_heads, t.head_dim
+    a = int(t.query_chunks[0])
+    n = int(t.chunk_tokens[a])
+    dev = v.device
+    qkv = torch.randn((n, 3, H, d), device=dev).to(torch.bfloat16)
+    th = torch.rand((n, d // 2), device=dev) * 6.283185307179586
+    cos_t, sin_t = torch.cos(th), torch.sin(th)
+    e4m3 = k8_pool is not None
+    q_out = None if e4m3 else torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    q8 = torch.empty((n, H, d), dtype=torch.uint8, device=dev) if e4m3 else None
+    qs = torch.empty(((n + 63) // 64, H), dtype=torch.float32, device=dev) if e4m3 else None
+    kp = None if e4m3 else k_pool.clone()
+    k8p = k8_pool.clone() if e4m3 else None
+    ksp = k_scale.clone() if e4m3 else None
+    vp = v.clone()
+
+    def call():
+        B.wfattn_rope_publish(att.plan, a, qkv, cos_t, sin_t, q_out, q8, qs, kp, k8p, ksp, vp, None, 0, att.ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    elems = n * H * d
+    nbytes = 3 * elems * 2 + 2 * n * (d // 2) * 4 + elems * (1 if e4m3 else 2) + elems * (1 if e4m3 else 2) + elems * 2
+    return {"rope_publish": {"chunk_tokens": n, "q_and_k": "e4m3" if e4m3 else "bf16", "ms": round(ms, 4),
+                             "bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(nbytes / (ms * 1e-3) / 8e12, 4)}}
+
+
 def publish_fp8(B, att, t, q, k8, ks, v, reps: int = 20):
     """Outside the timed steps: wfattn_publish_kv_fp8 of the query chunk (K quantized to e4m3 per
     64-token block and head into the K8 pool, V copied), HBM-bound: 2 B read + 1 B written per K
@@ -337,6 +378,7 @@ def main():
     extra = {}
     if not (f32 or args.no_extras):
         extra = publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v)
+        extra.update(rope_publish(B, att, t, None if fp8 else k, k8 if fp8 else None, ks if fp8 else None, v))
     ms = float(per.mean())
     flops = effective_flops(t)
     tflops = flops / (ms * 1e-3) / 1e12

@@ -21,7 +21,7 @@ WFATTN_WS_BF16, WFATTN_WS_FP32, WFATTN_WS_FP8 = 0, 1, 2
 EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_workspace_bytes",
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
-            "wfattn_fwd_gated", "wfattn_publish_kv_fp8"]
+            "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 
 
@@ -81,6 +81,9 @@ def lib():
         L.wfattn_fwd_gated.restype = i32
         L.wfattn_publish_kv_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
         L.wfattn_publish_kv_fp8.restype = i32
+        L.wfattn_rope_publish.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz,
+                                          vp]
+        L.wfattn_rope_publish.restype = i32
         L.wfattn_status_str.argtypes = [i32]
         L.wfattn_status_str.restype = ctypes.c_char_p
         L.wfattn_abi_version.argtypes = []
@@ -193,6 +196,14 @@ def wfattn_publish_kv_fp8(plan: Plan, chunk: int, k_src, v_src, k8_pool, k_scale
                                        _ptr(k_scale), _ptr(v_pool), _ptr(flags), int(generation) & 0xffffffff,
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "wfattn_publish_kv_fp8")
+
+
+def wfattn_rope_publish(plan: Plan, chunk: int, qkv, cos_t, sin_t, q_out, q8, q_scale, k_pool, k8_pool, k_scale,
+                        v_pool, flags, generation: int, ws, stream=None):
+    _check(lib().wfattn_rope_publish(plan.handle, int(chunk), _ptr(qkv), _ptr(cos_t), _ptr(sin_t), _ptr(q_out),
+                                     _ptr(q8), _ptr(q_scale), _ptr(k_pool), _ptr(k8_pool), _ptr(k_scale),
+                                     _ptr(v_pool), _ptr(flags), int(generation) & 0xffffffff, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "wfattn_rope_publish")
 
 
 def wfattn_fwd_gated(plan: Plan, q, k_pool, v_pool, out, lse, ws, flags, need, spin_limit: int, gate_status,

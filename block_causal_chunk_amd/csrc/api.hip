@@ -199,6 +199,47 @@ extern "C" wfattn_status wfattn_publish_kv_fp8(const wfattn_plan_t* plan, int32_
              : WFATTN_ERR_DEVICE;
 }
 
+extern "C" wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t chunk, const void* qkv,
+                                             const float* cos_t, const float* sin_t, void* q_out, uint8_t* q8,
+                                             float* q_scale, void* k_pool, uint8_t* k8_pool, float* k_scale,
+                                             void* v_pool, uint32_t* flags, uint32_t generation, const void* ws,
+                                             size_t ws_bytes, void* stream) {
+  if (!plan || !qkv || !cos_t || !sin_t || !v_pool) return WFATTN_ERR_NULL;
+  if (!k_pool == !k8_pool) return WFATTN_ERR_INVALID;  // exactly one form of K
+  if ((k8_pool && !k_scale) || (q8 && !q_scale)) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  const Plan* P = as_plan(plan);
+  if (chunk < 0 || chunk >= P->num_chunks) return WFATTN_ERR_INVALID;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(qkv, 16) || !aligned(cos_t, 16) || !aligned(sin_t, 16) || !aligned(q_out, 16) || !aligned(q8, 16) ||
+      !aligned(q_scale, 4) || !aligned(k_pool, 16) || !aligned(k8_pool, 16) || !aligned(k_scale, 4) ||
+      !aligned(v_pool, 16) || !aligned(flags, 4) || !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  RopeParams rp{};
+  rp.qkv = static_cast<const uint16_t*>(qkv);
+  rp.cos_t = cos_t;
+  rp.sin_t = sin_t;
+  rp.q_out = static_cast<uint16_t*>(q_out);
+  rp.q8 = q8;
+  rp.q_scale = q_scale;
+  rp.k_pool = static_cast<uint16_t*>(k_pool);
+  rp.k8_pool = k8_pool;
+  rp.k_scale = k_scale;
+  rp.v_pool = static_cast<uint16_t*>(v_pool);
+  rp.blob = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + P->ws_blob);
+  rp.chunk = chunk;
+  rp.heads = P->num_heads;
+  rp.nonce_lo = static_cast<uint32_t>(P->nonce & 0xffffffffu);
+  rp.nonce_hi = static_cast<uint32_t>(P->nonce >> 32);
+  rp.flags = flags;
+  rp.generation = generation;
+  const int64_t tokens = P->blob[P->off_chunks + static_cast<size_t>(chunk) * kChunkInts + 1];
+  return launch_rope_publish(rp, tokens, P->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? WFATTN_OK
+             : WFATTN_ERR_DEVICE;
+}
+
 extern "C" wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads, int32_t head_dim,
                                              uint8_t* x8, float* scales, void* stream) {
   if (!x_bf16 || !x8 || !scales) return WFATTN_ERR_NULL;

@@ -60,6 +60,25 @@ struct PublishFp8Params {
   uint32_t generation;
 };
 
+struct RopeParams {
+  const uint16_t* qkv;     // bf16 [tokens, 3, H, D]: q, k, v of a token side by side
+  const float* cos_t;      // [tokens, D/2]
+  const float* sin_t;      // [tokens, D/2]
+  uint16_t* q_out;         // bf16 [tokens, H, D] or nullptr
+  uint8_t* q8;             // e4m3 [tokens, H, D] or nullptr
+  float* q_scale;          // [ceil(tokens/64), H]
+  uint16_t* k_pool;        // bf16 pool, or nullptr when k8_pool is set
+  uint8_t* k8_pool;        // e4m3 pool, or nullptr
+  float* k_scale;          // [pool_rows / 64, H]
+  uint16_t* v_pool;        // bf16 pool
+  const int32_t* blob;
+  int32_t chunk;
+  int32_t heads;
+  uint32_t nonce_lo, nonce_hi;
+  uint32_t* flags;
+  uint32_t generation;
+};
+
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s);
 hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, int head_dim, bool out_f32, int groups, hipStream_t s);
@@ -67,6 +86,7 @@ hipError_t launch_publish(const PublishParams& p, int64_t tokens, hipStream_t s)
 // flags[chunk] = generation, release-ordered after everything before it on the stream
 hipError_t launch_flag(uint32_t* flags, int32_t chunk, uint32_t generation, hipStream_t s);
 hipError_t launch_publish_fp8(const PublishFp8Params& p, int64_t tokens, int32_t head_dim, hipStream_t s);
+hipError_t launch_rope_publish(const RopeParams& p, int64_t tokens, int32_t head_dim, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int32_t heads, int32_t head_dim,
                                uint8_t* x8, float* scales, hipStream_t s);

@@ -6,81 +6,12 @@
 // scale = amax/448, multiplier = 448/amax (both correctly rounded), y = x * multiplier clamped to
 // [-448, 448] (NaN kept), then the hardware round-to-nearest-even conversion, which is exact RNE
 // inside the clamp range; amax == 0 gives scale 1 and multiplier 1.
-#include "device.hpp"
+#include "blockq.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
 namespace wfattn {
 namespace {
-
-// One (64-row block, head): rows [0, nrows) of the block, row r of the source at
-// x + r * heads * D and of the codes at x8 + r * heads * D (this head's channels); the scale goes
-// to *scale.  Called by a whole 256-thread workgroup.
-template <int D>
-__device__ __forceinline__ void quantize_block(const uint16_t* __restrict__ x, int nrows, int heads,
-                                               uint8_t* __restrict__ x8, float* __restrict__ scale_out) {
-  constexpr int GPR = D / 8;            // 16-byte groups per row
-  constexpr int RPI = 256 / GPR;        // rows covered by the block per iteration
-  constexpr int ITER = 64 / RPI;
-  const int g = threadIdx.x % GPR, rsub = threadIdx.x / GPR;
-  float v[ITER][8];
-  float amax = 0.f;
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int r = it * RPI + rsub;
-    if (r < nrows) {
-      const uint4 w = *reinterpret_cast<const uint4*>(x + (size_t)r * heads * D + g * 8);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[it][2 * j] = __uint_as_float(u[j] << 16);
-        v[it][2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float a = fabsf(v[it][j]);
-        amax = (a > amax) ? a : amax;  // a NaN compares false and is ignored
-      }
-    }
-  }
-  // block max: wave shuffle, then across the 4 waves through LDS
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(amax, off);
-    amax = (o > amax) ? o : amax;
-  }
-  __shared__ float wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = wmax[0];
-#pragma unroll
-  for (int w = 1; w < 4; ++w) amax = (wmax[w] > amax) ? wmax[w] : amax;
-  float scale = 1.f, mult = 1.f;
-  if (amax > 0.f) {
-    scale = __fdiv_rn(amax, 448.f);
-    mult = __fdiv_rn(448.f, amax);
-  }
-  if (threadIdx.x == 0) *scale_out = scale;
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int r = it * RPI + rsub;
-    if (r < nrows) {
-      float y[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float t = __fmul_rn(v[it][j], mult);
-        t = (t > 448.f) ? 448.f : t;
-        t = (t < -448.f) ? -448.f : t;
-        y[j] = t;
-      }
-      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-      *reinterpret_cast<uint2*>(x8 + (size_t)r * heads * D + g * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
-    }
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* __restrict__ x, int64_t rows, int heads,

@@ -219,6 +219,31 @@ wfattn_status wfattn_publish_kv_fp8(const wfattn_plan_t* plan, int32_t chunk, co
                                     void* v_pool, uint32_t* flags, uint32_t generation,
                                     const void* ws, size_t ws_bytes, void* stream);
 
+/* Fused pre-attention epilogue of one chunk (the producer's step right after its QKV projection:
+ * project page, "03 - End-to-end KV transport", on publishing K/V as soon as they are projected,
+ * and "Precision", on requantization cost).  qkv: bf16 [chunk_tokens, 3, H, d], the projection
+ * output with q, k and v of a token side by side.  cos_t, sin_t: fp32 [chunk_tokens, d/2], the
+ * caller's rotary angles per token and channel pair (any positional scheme, e.g. one over frames,
+ * height and width).  Q and K are rotated pair by pair:
+ *   (x[2i], x[2i+1]) -> (x[2i] c - x[2i+1] s, x[2i] s + x[2i+1] c),
+ * every product and sum rounded to fp32 on its own (no fused multiply-add), then the result
+ * rounded to bf16 (RNE).  Outputs:
+ *   q_out   bf16 [chunk_tokens, H, d] (NULL: not written);
+ *   q8, q_scale  e4m3 codes of the rotated bf16 Q with one scale per (64-row block of the
+ *           chunk, head), as wfattn_quantize_fp8 (NULL: not written); pass the chunk's place in
+ *           the call's q8 / q_scale arrays;
+ *   K       rotated, into the chunk's pages: k_pool (bf16) or k8_pool + k_scale (e4m3 as
+ *           wfattn_publish_kv_fp8) -- exactly one of k_pool and k8_pool;
+ *   V       unchanged, into the chunk's pages of v_pool;
+ *   flags   as wfattn_publish_kv.
+ * Errors: NULL, INVALID (bad plan, chunk out of range, both or neither of k_pool and k8_pool),
+ * UNSUPPORTED (alignment: 16 bytes, scales 4), WORKSPACE, DEVICE. */
+wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t chunk, const void* qkv,
+                                  const float* cos_t, const float* sin_t, void* q_out, uint8_t* q8,
+                                  float* q_scale, void* k_pool, uint8_t* k8_pool, float* k_scale,
+                                  void* v_pool, uint32_t* flags, uint32_t generation,
+                                  const void* ws, size_t ws_bytes, void* stream);
+
 /* Upper bound of spin_limit in wfattn_fwd_gated: one poll is followed by a sleep of about 4000
  * clocks, so a gate gives up after about 2 s at most. */
 #define WFATTN_GATE_SPIN_MAX (1 << 20)

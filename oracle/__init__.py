@@ -137,6 +137,22 @@ def publish_kv(table, chunk: int, k_src, v_src, k_pool, v_pool):
     return kp, vp
 
 
+def rotate_pairs(x, cos_t, sin_t):
+    """Rotary embedding of x [tokens, H, d] (any float; widened exactly to float32) by per-token,
+    per-pair angles given as cos_t, sin_t [tokens, d/2]: channel pair (2i, 2i+1) becomes
+    (x0 c - x1 s, x0 s + x1 c).  Each product and each sum is one float32 operation (numpy
+    float32 arithmetic rounds every operation to nearest-even; nothing is fused), so the result is
+    the float32 value of that formula.  Returns float32 [tokens, H, d]."""
+    x = np.asarray(x, dtype=np.float32)
+    c = np.asarray(cos_t, dtype=np.float32)[:, None, :]
+    s = np.asarray(sin_t, dtype=np.float32)[:, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = (x0 * c) - (x1 * s)
+    out[..., 1::2] = (x0 * s) + (x1 * c)
+    return out
+
+
 def attn_masked(q, k, v, allowed, scale: float, nthreads: int = 0):
     """One head, explicit mask: q [nq, d], k/v [nk, d], allowed [nq, nk] bool."""
     qd, kd, vd = _f64(q), _f64(k), _f64(v)

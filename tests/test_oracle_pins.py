@@ -5,7 +5,8 @@ case, P4 closed forms, P5 permutation/page-shuffle invariance, P6 no reverse edg
 decomposition of a multi-chunk query set, P8 the e4m3 codec against the OCP definition and
 torch's float8_e4m3fn, P9 merging key partitions through their LSEs, P10 ties in chunk order (full
 attention when all tie, a tie group equals one merged chunk, SDPA), P11 placing a chunk's K/V
-into its pages (round trip through the dense gather, rebuilding the input pool), plus brute force on tiny
+into its pages (round trip through the dense gather, rebuilding the input pool), P12 the rotary
+embedding (special angles, complex multiplication), plus brute force on tiny
 inputs, a hand-derived closed-form fixture, and checks that plausible mistakes would be caught.
 """
 import json
@@ -187,6 +188,36 @@ def test_p11_publishing_every_chunk_rebuilds_the_input_pool(oracle_lib):
         kp, vp = oracle_lib.publish_kv(c.table, b, gk[owner == b], gv[owner == b], kp, vp)
     same = lambda a, b: ((a == b) | (np.isnan(a) & np.isnan(b))).all()
     assert same(kp, c.k_pool.double().numpy()) and same(vp, c.v_pool.double().numpy())
+
+
+# ---------------------------------------------------------------- P12: rotary embedding
+def _angles(rng, n, half):
+    th = rng.uniform(-np.pi, np.pi, size=(n, half))
+    return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32), th
+
+
+def test_p12_rotation_special_angles(oracle_lib):
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((5, 3, 16)).astype(np.float32)
+    one, zero = np.ones((5, 8), np.float32), np.zeros((5, 8), np.float32)
+    assert np.array_equal(oracle_lib.rotate_pairs(x, one, zero), x)  # no rotation
+    q = oracle_lib.rotate_pairs(x, zero, one)  # a quarter turn: (x0, x1) -> (-x1, x0)
+    assert np.array_equal(q[..., 0::2], -x[..., 1::2]) and np.array_equal(q[..., 1::2], x[..., 0::2])
+
+
+def test_p12_rotation_is_complex_multiplication(oracle_lib):
+    """Against an independent statement: pair (x0, x1) as the complex number x0 + i x1, times
+    exp(i theta), in complex128; the float32 formula stays within its rounding of it."""
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((40, 2, 32)).astype(np.float32)
+    c, s_, th = _angles(rng, 40, 16)
+    got = oracle_lib.rotate_pairs(x, c, s_).astype(np.float64)
+    z = (x[..., 0::2].astype(np.float64) + 1j * x[..., 1::2]) * (c.astype(np.float64) + 1j * s_)[:, None, :]
+    bound = 3 * 2.0 ** -24 * (np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])).astype(np.float64)
+    assert (np.abs(got[..., 0::2] - z.real) <= bound).all() and (np.abs(got[..., 1::2] - z.imag) <= bound).all()
+    # and by theta then -theta is the identity up to that rounding
+    back = oracle_lib.rotate_pairs(oracle_lib.rotate_pairs(x, c, s_), c, -s_).astype(np.float64)
+    assert np.abs(back - x).max() <= 1e-5 * np.abs(x).max()
 
 
 # ---------------------------------------------------------------- P3: single chunk

@@ -152,6 +152,15 @@ def test_call_errors_before_any_hip_call(B):
     assert P8(h, 1, A, A, A, A + 2, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
     assert P8(h, 1, A, A, A + 8, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
     assert P8(h, 1, A, A, A, A, A, A, 3, None, ws_need, None) == B.WFATTN_ERR_WORKSPACE
+    R = L.wfattn_rope_publish
+    assert R(h, 1, None, A, A, A, A, A, A, None, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL
+    assert R(h, 1, A, A, A, A, A, A, A, A, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID  # both K forms
+    assert R(h, 1, A, A, A, A, A, A, None, None, A, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID  # neither
+    assert R(h, 1, A, A, A, A, A, None, A, None, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL  # q8, no scale
+    assert R(h, 1, A, A, A, A, None, None, None, A, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_NULL  # k8, no scale
+    assert R(h, 9, A, A, A, A, None, None, A, None, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID
+    assert R(h, 1, A, A + 8, A, A, None, None, A, None, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert R(h, 1, A, A, A, A, None, None, A, None, None, A, A, 3, A, 8, None) == B.WFATTN_ERR_WORKSPACE
     # the gated forward
     G = L.wfattn_fwd_gated
     assert G(h, A, A, A, A, None, A, ws_need, None, A, 0, A, None) == B.WFATTN_ERR_NULL
