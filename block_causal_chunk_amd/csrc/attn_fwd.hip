@@ -1,4 +1,5 @@
-// attn_fwd.hip -- block-causal chunk attention forward, bf16 MFMA (gfx950).
+// attn_fwd.hip -- block-causal chunk attention forward on gfx950 MFMA (bf16, or e4m3 for the
+// scores), the merge of split key ranges, and the fp32 -> bf16 staging of fp32 I/O.
 //
 // What one workgroup computes: segments of work items, one item = (head, query tile of up to
 // 256 rows of one query chunk, that chunk's visible key tiles).  The visible keys are the chunk's
@@ -16,6 +17,9 @@
 //   softmax             : P = exp2(S * c - m) in fp32 against a fixed per-row reference m
 //   O^T += V^T . P^T    : P stays in registers as the B operand; V^T comes from LDS through
 //                         ds_read_b64_tr_b16 transposed reads; O lives in AGPRs
+//
+// Kernel instances: head_dim 64 / 128 x {bf16 out, fp32 out, e4m3 scores, gated bf16 out}; the
+// gated instance first checks, per item, the generation flags of the chunks it reads (gate_item).
 //
 // The key loop is software-pipelined in half tiles (32 keys).  One half step issues the score
 // MFMAs of the next half and the P.V MFMAs of the previous half, one at a time, and between two
