@@ -310,6 +310,26 @@ def test_schedule_random_tables_with_ties(B):
     assert int(tiles[:int(items[0][5]), 1].sum()) == 100 + 64 + 200 + 130 + 90
 
 
+def test_chunk_table_of_the_plan(B):
+    """describe(6): per chunk its first key tile, tokens, rank in clean -> noisy order and the last
+    rank it sees; with ties, every chunk of a tie group sees to the group's end.  Items carry the
+    last rank their query chunk sees (the gate's range)."""
+    t = make_table([100, 64, 200, 130, 90, 70], [0, 1, 2, 2, 2, 3], [4, 2, 5], 64, 1, 128)
+    plan = B.wfattn_plan(t, order_ties=1)
+    ch = plan.describe(6).reshape(-1, 4)
+    tiles = plan.describe(2).reshape(-1, 2)
+    items = plan.describe(1).reshape(-1, 8)
+    assert ch[:, 1].tolist() == [100, 64, 200, 130, 90, 70]
+    assert ch[:, 2].tolist() == [0, 1, 2, 3, 4, 5]  # ranks: by order, ties by chunk id
+    assert ch[:, 3].tolist() == [0, 1, 4, 4, 4, 5]
+    for c in range(6):  # a chunk's tiles start at its first tile and cover its tokens
+        n = -(-int(t.chunk_tokens[c]) // 64)
+        assert int(tiles[ch[c, 0]:ch[c, 0] + n, 1].sum()) == int(t.chunk_tokens[c])
+    for it in items:
+        a = int(t.query_chunks[it[4]])
+        assert it[6] == ch[a, 3]
+
+
 def test_schedule_full_size_tables_and_xcd_grouping(B):
     """The five workloads' tables (sizes only; no values are drawn): coverage, balance across
     the 256 workgroups and the 8 XCDs, and few heads per XCD."""
