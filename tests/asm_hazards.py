@@ -8,7 +8,9 @@ order (straight-line, conservatively ignoring that a taken branch adds distance)
   RAW  an MFMA writes registers that a later VALU instruction (including v_accvgpr_read/mov)
        reads before the result is ready;
   WAR  a later VALU instruction overwrites an MFMA's accumulator input (SrcC) while the MFMA
-       may still be reading it.
+       may still be reading it;
+  OPND an MFMA reads as an operand a register that a VALU instruction wrote fewer than 2 wait
+       states before.
 
 Wait states: every instruction counts one, s_nop N counts N + 1.  Requirements for gfx950, the
 ones the compiler itself inserts after the builtin forms: 12 after a 32x32x16 bf16 MFMA (8
@@ -18,6 +20,9 @@ from __future__ import annotations
 
 import re
 
+# A VALU write (v_accvgpr_write/mov included) of a register an MFMA then reads as SrcA/B/C needs 2
+# wait states in between (what the compiler inserts, as s_nop 1, before its own MFMA builtins).
+OPND_NEED = 2
 RAW_NEED = {"v_mfma_f32_32x32x16_bf16": 12, "v_mfma_f32_32x32x64_f8f6f4": 20}
 WAR_NEED = {"v_mfma_f32_32x32x16_bf16": 8, "v_mfma_f32_32x32x64_f8f6f4": 16}
 
@@ -41,6 +46,7 @@ def kernel_body(asm: str, name: str):
 def check(lines):
     """Returns a list of (kind, mfma line, offending line, missing wait states)."""
     raw, war, found = [], [], []
+    opnd = []  # recent VALU writes: an MFMA may read them as an operand only OPND_NEED wait states later
     for ln, l in enumerate(lines):
         if not l or l.endswith(":") or l.startswith("."):
             continue
@@ -60,6 +66,13 @@ def check(lines):
         elif op.startswith(("ds_write", "global_store", "buffer_store", "scratch_store")):
             for a in args:
                 reads |= _regs(a)
+        if op in RAW_NEED:
+            srcs = set()
+            for x in args[1:4]:
+                srcs |= _regs(x)
+            for rem, rs, src in opnd:
+                if rem > 0 and rs & srcs:
+                    found.append(("OPND", l, lines[src], rem))
         for rem, rs, src in raw:
             if rem > 0 and rs & reads:
                 found.append(("RAW", lines[src], l, rem))
@@ -68,6 +81,9 @@ def check(lines):
                 found.append(("WAR", lines[src], l, rem))
         raw = [(r - ws, rs, s) for r, rs, s in raw if r - ws > 0]
         war = [(r - ws, rs, s) for r, rs, s in war if r - ws > 0]
+        opnd = [(r - ws, rs, s) for r, rs, s in opnd if r - ws > 0]
+        if op.startswith("v_") and not op.startswith("v_mfma") and writes:
+            opnd.append((OPND_NEED, writes, ln))
         if op in RAW_NEED:
             raw.append((RAW_NEED[op], _regs(args[0]), ln))
             if len(args) >= 4:

@@ -43,3 +43,7 @@ def test_checker_finds_a_planted_hazard():
     assert check(lines[:1] + ["s_nop 7", "s_nop 3", lines[2]]) == []
     war = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], a[4:7], v[0:15]", "v_mov_b32 v3, 0"]
     assert [f[0] for f in check(war)] == ["WAR"]
+    # a VALU write of an MFMA operand right before it (the constant the compiler rematerialised)
+    opnd = ["v_mov_b64_e32 v[8:9], s[98:99]", "v_mfma_f32_32x32x16_bf16 a[0:15], v[6:9], v[20:23], a[0:15]"]
+    assert [f[0] for f in check(opnd)] == ["OPND"]
+    assert check(opnd[:1] + ["s_nop 1"] + opnd[1:]) == []
