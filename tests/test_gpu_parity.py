@@ -278,6 +278,46 @@ def test_gate_skips_items_of_unpublished_chunks(B, O):
     check_bf16(f64(out), ref, "gate-open")
 
 
+def test_pool_beyond_4gib(B, O):
+    """64-bit addressing: K and V pools of 8400 pages x 256 tokens x 8 heads x 128 bf16 (4.4 GB
+    each), with every chunk's pages placed past the first 4 GiB.  The forward reads them and the
+    publish kernel writes one of them there; the oracle sees a compact copy of just those pages."""
+    rng = np.random.default_rng(91)
+    H, d, P, NP = 8, 128, 256, 8400
+    tokens, order = [300, 130, 257], [0, 1, 2]
+    compact = make_table(tokens, order, [2], P, H, d, shuffle_rng=rng, spare=0)
+    c = fill_case("big", compact, rng, torch.bfloat16)
+    n_log = int(compact.page_offsets[-1])
+    high = 8192 + rng.permutation(NP - 8192)[:n_log]  # physical pages past byte 2^32 of each pool
+    big = compact.copy()
+    big.num_pages = NP
+    big.page_ids = high.astype(np.int32)  # logical page lp lives in physical page high[lp]
+    kp = torch.empty((NP, P, H, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty((NP, P, H, d), dtype=torch.bfloat16, device="cuda")
+    for lp in range(n_log):  # logical page lp: compact physical compact.page_ids[lp] -> high[lp]
+        kp[int(big.page_ids[lp])] = c.k_pool[int(compact.page_ids[lp])].cuda()
+        vp[int(big.page_ids[lp])] = c.v_pool[int(compact.page_ids[lp])].cuda()
+    assert int(big.page_ids.min()) * P * H * d * 2 >= 2 ** 32
+    att = B.Attention(big)
+    print("[case] pools of 4.4 GB, pages past 4 GiB", flush=True)
+    out, lse = att.fwd(c.q.cuda(), kp, vp, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.attn_rows(compact, c.q, c.k_pool, c.v_pool)
+    check_bf16(f64(out), ref, "beyond 4 GiB")
+    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    # publish chunk 1 (130 tokens, one page) into its high page and read the page back
+    sk, sv = _chunk_rows(c, 1)
+    page = int(big.page_ids[int(big.page_offsets[1])])
+    kp[page].zero_()
+    vp[page].zero_()
+    B.wfattn_publish_kv(att.plan, 1, sk.cuda(), sv.cuda(), kp, vp, None, 0, att.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kp[page][:130].cpu().view(torch.int16), sk.view(torch.int16))
+    assert torch.equal(vp[page][:130].cpu().view(torch.int16), sv.view(torch.int16))
+    del kp, vp
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ invariants (bitwise)
 def test_page_shuffle_is_bitwise_identical(B):
     c = medium_case("long_rollout", seed=5)
