@@ -151,6 +151,49 @@ def test_tied_window(B, O):
             assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
 
 
+def test_tied_window_e4m3_and_gated(B, O):
+    """Ties combined with the e4m3 forward (against the oracle on dequantized inputs) and with the
+    gate: one chunk of the tied window one generation short skips every window item (they all see
+    it), while a query chunk outside the window is exact."""
+    rng = np.random.default_rng(47)
+    H, d = 2, 128
+    tok, order = [64, 100, 96, 130, 70, 90], [0, 1, 2, 2, 2, 3]
+    t = make_table(tok, order, [4, 2, 3, 1], 64, H, d, shuffle_rng=rng, spare=2)
+    c = fill_case("tied8", t, rng, torch.bfloat16)
+    q, k, v = to_dev(c)
+    # e4m3 scores over a tied plan
+    att8 = B.Attention(t, mode=B.WFATTN_WS_FP8, order_ties=1)
+    rows = k.shape[0] * k.shape[1]
+    k8, ks = B.quantize_fp8(k.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(t, q)
+    print("[case] tied window, e4m3 scores", flush=True)
+    out8, _ = att8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v)
+    torch.cuda.synchronize()
+    qdq, kdq = _dequantized_case(O, c)
+    ref_dq, _ = O.attn_rows(t, qdq, kdq, c.v_pool)
+    check_bf16(f64(out8), ref_dq, "tied e4m3 (dequantized oracle)")
+    # gate over a tied plan: chunk 3 (in the window of order 2) is short
+    att = B.Attention(t, split_k=1, order_ties=1)
+    need = torch.full((t.num_chunks,), 4, dtype=torch.int32, device="cuda")
+    flags = need.clone()
+    flags[3] = 3
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((t.lq, H, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    print("[case] tied window, gate with one window chunk short", flush=True)
+    B.wfattn_fwd_gated(att.plan, q, k, v, out, None, att.ws, flags, need, 2, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    ref, _ = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+    qstart = np.concatenate([[0], np.cumsum([tok[a] for a in t.query_chunks])])
+    got = f64(out)
+    for i, a in enumerate(t.query_chunks):
+        r0, r1 = qstart[i], qstart[i + 1]
+        if order[a] == 2:  # a window chunk: it sees chunk 3
+            assert (got[r0:r1] == 7.0).all(), a
+        else:              # chunk 1 (order 1) does not see the window
+            check_bf16(got[r0:r1], ref[r0:r1], f"gate outside the window ({a})")
+
+
 def test_store_rank_query_shape(B, O):
     """The store step re-runs the finished chunk over its clean context: the query is the store
     chunk (after a sink and a clean history), while four noisier chunks still in flight sit in the
