@@ -397,7 +397,7 @@ def main():
               "kv_unique_bytes": unique, "kv_unique_gbs": round(unique / sec / 1e9, 1),
               "beyond_l2_gbs": None if traffic is None else round(traffic / sec / 1e9, 1)}
     res = {
-        "metric": "effective attention TFLOP/s (unmasked pairs only) + chunk-tasks/s, % of MFMA peak",
+        "metric": "effective attention TFLOP/s + chunk-tasks/s, Wan-1.3B shape, % MFMA peak",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
