@@ -66,9 +66,10 @@ def kernel_src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """Beyond-L2 bytes per call (attention + merge launches) from the committed rocprofv3 counter
-    summary, if it was taken with the current kernel sources; else None."""
+def traffic_from_profiles(workload: str, kernel: str = ""):
+    """Beyond-L2 bytes per call (attention + merge launches), or per launch of `kernel`, from the
+    committed rocprofv3 counter summary, if it was taken with the current kernel sources; else
+    None."""
     p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.json")
     if not os.path.exists(p):
         return None
@@ -78,6 +79,9 @@ def traffic_from_profiles(workload: str):
         return None
     if d.get("kernel_src_sha") != kernel_src_hash():
         return None
+    if kernel:
+        k = d.get("kernels", {}).get(kernel)
+        return None if k is None else k["fetch_bytes"] + k["write_bytes"]
     return d.get("hbm_bytes_per_call")
 
 
@@ -348,9 +352,17 @@ def main():
 
         def step():
             B.wfattn_fwd_fp8(att.plan, q8, qs, k8, ks, v, out, None, att.ws)
+
+        def step_marked(ev):
+            B.wfattn_fwd_fp8_marked(att.plan, q8, qs, k8, ks, v, out, None, att.ws, ev.cuda_event)
     else:
+        dt = B.WFATTN_FP32 if f32 else B.WFATTN_BF16
+
         def step():
-            B.wfattn_fwd(att.plan, B.WFATTN_FP32 if f32 else B.WFATTN_BF16, q, k, v, out, None, att.ws)
+            B.wfattn_fwd(att.plan, dt, q, k, v, out, None, att.ws)
+
+        def step_marked(ev):
+            B.wfattn_fwd_marked(att.plan, dt, q, k, v, out, None, att.ws, ev.cuda_event)
 
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     for _ in range(args.warmup):
@@ -358,12 +370,18 @@ def main():
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # one more event per step, recorded by the library between the attention launch and the merge
+    # launch (recorded once here so that it exists), to time the attention kernel on its own
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for ev in mids:
+        ev.record()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if scratch is not None:
             scratch.fill_(i & 0xFF)  # untimed 512 MB write evicts the Infinity Cache
         starts[i].record()
-        step()
+        step_marked(mids[i])
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -375,13 +393,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
+    per_attn = np.array([s.elapsed_time(m) for s, m in zip(starts, mids)])  # the attention kernel alone
     extra = {}
     if not (f32 or args.no_extras):
         extra = publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v)
         extra.update(rope_publish(B, att, t, None if fp8 else k, k8 if fp8 else None, ks if fp8 else None, v))
     ms = float(per.mean())
+    attn_ms = float(per_attn.mean())
     flops = effective_flops(t)
-    tflops = flops / (ms * 1e-3) / 1e12
+    tflops = flops / (ms * 1e-3) / 1e12  # the whole call (attention + merge): the metric's value
+    kflops = flops / (attn_ms * 1e-3) / 1e12
     tasks = len(t.query_chunks) / (float(np.median(per)) * 1e-3)  # per the p50 call
     peak = PEAK_MIXED if fp8 else PEAK_BF16
     staged, unique = gather_bytes(t, 1 if fp8 else 2)
@@ -390,7 +411,7 @@ def main():
     if counters is not None:
         # the roofline peak again at the clock the kernel actually ran at under load
         counters["peak_at_active_clock"] = round(peak * counters["active_clock_ghz"] / 2.4, 1)
-        counters["frac_at_active_clock"] = round(tflops / counters["peak_at_active_clock"], 4)
+        counters["frac_at_active_clock"] = round(kflops / counters["peak_at_active_clock"], 4)
     traffic = traffic_from_profiles(args.workload)
     sec = ms * 1e-3
     gather = {"lds_staged_bytes": staged, "lds_staged_gbs": round(staged / sec / 1e9, 1),
@@ -421,8 +442,11 @@ def main():
         "plan_and_upload_ms": round(plan_ms, 3),
         "plan": {"items": int(summary[0]), "key_tiles": int(summary[1]), "merge_groups": int(summary[2]),
                  "splits": int(summary[6]), "block_m": int(summary[4]), "block_n": int(summary[5])},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        # the dominant kernel: effective FLOPs over the attention kernel's own event-timed duration
+        "roofline": {"bound": "mfma", "achieved": round(kflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kflops / peak, 4), "traffic": traffic_from_profiles(args.workload, "attn_fwd_kernel"),
+                     "kernel": "attn_fwd_kernel",
+                     "kernel_ms": round(attn_ms, 4), "merge_ms": round(ms - attn_ms, 4)},
         "mfma_counters": counters,
         "exps_per_s": round(exps / (ms * 1e-3), 1),
         "gather": gather,

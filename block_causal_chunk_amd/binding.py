@@ -21,7 +21,8 @@ WFATTN_WS_BF16, WFATTN_WS_FP32, WFATTN_WS_FP8 = 0, 1, 2
 EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_workspace_bytes",
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
-            "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish"]
+            "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish", "wfattn_fwd_marked",
+            "wfattn_fwd_fp8_marked"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 
 
@@ -73,6 +74,10 @@ def lib():
         L.wfattn_fwd.restype = i32
         L.wfattn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.wfattn_fwd_fp8.restype = i32
+        L.wfattn_fwd_marked.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.wfattn_fwd_marked.restype = i32
+        L.wfattn_fwd_fp8_marked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.wfattn_fwd_fp8_marked.restype = i32
         L.wfattn_quantize_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.wfattn_quantize_fp8.restype = i32
         L.wfattn_publish_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
@@ -211,6 +216,19 @@ def wfattn_fwd_gated(plan: Plan, q, k_pool, v_pool, out, lse, ws, flags, need, s
     _check(lib().wfattn_fwd_gated(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(ws),
                                   ws.numel() * ws.element_size(), _ptr(flags), _ptr(need), int(spin_limit),
                                   _ptr(gate_status), _stream(stream)), "wfattn_fwd_gated")
+
+
+def wfattn_fwd_marked(plan: Plan, dtype: int, q, k_pool, v_pool, out, lse, ws, attn_done_event: int, stream=None):
+    _check(lib().wfattn_fwd_marked(plan.handle, int(dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
+                                   _ptr(ws), ws.numel() * ws.element_size(), attn_done_event, _stream(stream)),
+           "wfattn_fwd_marked")
+
+
+def wfattn_fwd_fp8_marked(plan: Plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, attn_done_event: int,
+                          stream=None):
+    _check(lib().wfattn_fwd_fp8_marked(plan.handle, _ptr(q8), _ptr(q_scale), _ptr(k8_pool), _ptr(k_scale),
+                                       _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                       attn_done_event, _stream(stream)), "wfattn_fwd_fp8_marked")
 
 
 def wfattn_quantize_fp8(x, rows: int, heads: int, head_dim: int, x8, scales, stream=None):

@@ -51,7 +51,7 @@ struct Gate {
 
 wfattn_status fwd_impl(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q, const void* k_pool,
                        const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
-                       const Gate* gate) {
+                       const Gate* gate, hipEvent_t mark = nullptr) {
   if (!plan || !q || !k_pool || !v_pool || !out) return WFATTN_ERR_NULL;
   if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
   if (dtype != WFATTN_BF16 && dtype != WFATTN_FP32) return WFATTN_ERR_UNSUPPORTED;
@@ -92,7 +92,34 @@ wfattn_status fwd_impl(const wfattn_plan_t* plan, wfattn_dtype dtype, const void
     fp.v = static_cast<const uint16_t*>(v_pool);
   }
   if (launch_attn_bf16(fp, P->head_dim, f32, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (mark && hipEventRecord(mark, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (launch_combine(fp, P->head_dim, f32, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  return WFATTN_OK;
+}
+
+wfattn_status fwd8_impl(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale, const uint8_t* k8_pool,
+                        const float* k_scale, const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes,
+                        void* stream, hipEvent_t mark) {
+  if (!plan || !q8 || !q_scale || !k8_pool || !k_scale || !v_pool || !out) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(q8, 16) || !aligned(k8_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) || !aligned(q_scale, 4) ||
+      !aligned(k_scale, 4) || !aligned(lse, 4) || !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  const Plan* P = as_plan(plan);
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FwdParams fp = base_params(P, ws);
+  fp.q8 = q8;
+  fp.q_scale = q_scale;
+  fp.k8 = k8_pool;
+  fp.k_scale = k_scale;
+  fp.v = static_cast<const uint16_t*>(v_pool);
+  fp.out = out;
+  fp.lse = lse;
+  if (launch_attn_fp8(fp, P->head_dim, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (mark && hipEventRecord(mark, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  if (launch_combine(fp, P->head_dim, false, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   return WFATTN_OK;
 }
 
@@ -145,26 +172,24 @@ extern "C" wfattn_status wfattn_publish_kv(const wfattn_plan_t* plan, int32_t ch
 extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
                                         const uint8_t* k8_pool, const float* k_scale, const void* v_pool, void* out,
                                         float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (!plan || !q8 || !q_scale || !k8_pool || !k_scale || !v_pool || !out) return WFATTN_ERR_NULL;
-  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
-  if (!ws) return WFATTN_ERR_WORKSPACE;
-  if (!aligned(q8, 16) || !aligned(k8_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) || !aligned(q_scale, 4) ||
-      !aligned(k_scale, 4) || !aligned(lse, 4) || !aligned(ws, 256))
-    return WFATTN_ERR_UNSUPPORTED;
-  const Plan* P = as_plan(plan);
-  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  FwdParams fp = base_params(P, ws);
-  fp.q8 = q8;
-  fp.q_scale = q_scale;
-  fp.k8 = k8_pool;
-  fp.k_scale = k_scale;
-  fp.v = static_cast<const uint16_t*>(v_pool);
-  fp.out = out;
-  fp.lse = lse;
-  if (launch_attn_fp8(fp, P->head_dim, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
-  if (launch_combine(fp, P->head_dim, false, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
-  return WFATTN_OK;
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" wfattn_status wfattn_fwd_marked(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
+                                           const void* k_pool, const void* v_pool, void* out, float* lse, void* ws,
+                                           size_t ws_bytes, void* attn_done_event, void* stream) {
+  if (!attn_done_event) return WFATTN_ERR_NULL;
+  return fwd_impl(plan, dtype, q, k_pool, v_pool, out, lse, ws, ws_bytes, stream, nullptr,
+                  static_cast<hipEvent_t>(attn_done_event));
+}
+
+extern "C" wfattn_status wfattn_fwd_fp8_marked(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                                               const uint8_t* k8_pool, const float* k_scale, const void* v_pool,
+                                               void* out, float* lse, void* ws, size_t ws_bytes,
+                                               void* attn_done_event, void* stream) {
+  if (!attn_done_event) return WFATTN_ERR_NULL;
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream,
+                   static_cast<hipEvent_t>(attn_done_event));
 }
 
 extern "C" wfattn_status wfattn_publish_kv_fp8(const wfattn_plan_t* plan, int32_t chunk, const void* k_src,

@@ -176,6 +176,18 @@ wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const
                              const uint8_t* k8_pool, const float* k_scale, const void* v_pool,
                              void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement aid: wfattn_fwd and wfattn_fwd_fp8 with one more argument, a hipEvent_t (passed
+ * as void*, created by the caller) that is recorded on `stream` between the attention launch and
+ * the launch of the merge of split key ranges, so that the two can be timed apart with events.
+ * Otherwise identical.  Errors: as wfattn_fwd / wfattn_fwd_fp8, plus NULL (no event). */
+wfattn_status wfattn_fwd_marked(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
+                                const void* k_pool, const void* v_pool, void* out, float* lse,
+                                void* ws, size_t ws_bytes, void* attn_done_event, void* stream);
+wfattn_status wfattn_fwd_fp8_marked(const wfattn_plan_t* plan, const uint8_t* q8,
+                                    const float* q_scale, const uint8_t* k8_pool,
+                                    const float* k_scale, const void* v_pool, void* out, float* lse,
+                                    void* ws, size_t ws_bytes, void* attn_done_event, void* stream);
+
 /* Block quantizer: x_bf16 [rows, heads, head_dim] -> x8 (e4m3 codes, same shape) and
  * scales [ceil(rows/64), heads].  For each block of 64 consecutive rows (the last may be short)
  * and head: amax = max |x| over the block (NaN ignored), scale = amax/448, code = round-to-

@@ -448,6 +448,39 @@ def test_stale_workspace_is_ignored(B):
     assert (out == 7.0).all()
 
 
+def test_marked_forwards_equal_unmarked(B):
+    """The marked variants (an event recorded between the attention launch and the merge launch)
+    return the same bits as the plain forwards, and the event falls inside the call."""
+    c = make_case("wan13b_task", small=True)
+    q, k, v = to_dev(c)
+    H, d = c.table.num_heads, c.table.head_dim
+    print("[case] marked bf16 / e4m3 split_k=3", flush=True)
+    att = B.Attention(c.table, split_k=3)
+    o1, l1 = att.fwd(q, k, v, want_lse=True)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    t0, mid, t1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    mid.record()  # torch creates the HIP event at its first record
+    t0.record()
+    B.wfattn_fwd_marked(att.plan, B.WFATTN_BF16, q, k, v, o2, l2, att.ws, mid.cuda_event)
+    t1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert 0.0 <= t0.elapsed_time(mid) <= t0.elapsed_time(t1)
+
+    rows = k.shape[0] * k.shape[1]
+    k8, ks = B.quantize_fp8(k.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(c.table, q)
+    a8 = B.Attention(c.table, mode=B.WFATTN_WS_FP8, split_k=3)
+    p1, m1 = a8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, want_lse=True)
+    p2, m2 = torch.empty_like(p1), torch.empty_like(m1)
+    t0.record()
+    B.wfattn_fwd_fp8_marked(a8.plan, q8, qs, k8.view(k.shape), ks, v, p2, m2, a8.ws, mid.cuda_event)
+    t1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(m1, m2)
+    assert 0.0 <= t0.elapsed_time(mid) <= t0.elapsed_time(t1)
+
+
 # ------------------------------------------------------------------ fp8
 def _quant_compare(O, x_cpu, codes_gpu, scales_gpu):
     ref8, ref_sc = O.quantize_e4m3(x_cpu)

@@ -161,6 +161,11 @@ def test_call_errors_before_any_hip_call(B):
     assert R(h, 9, A, A, A, A, None, None, A, None, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_INVALID
     assert R(h, 1, A, A + 8, A, A, None, None, A, None, None, A, A, 3, A, ws_need, None) == B.WFATTN_ERR_UNSUPPORTED
     assert R(h, 1, A, A, A, A, None, None, A, None, None, A, A, 3, A, 8, None) == B.WFATTN_ERR_WORKSPACE
+    # the marked forwards (an event between the attention and the merge launches)
+    assert L.wfattn_fwd_marked(h, 0, A, A, A, A, None, A, ws_need, None, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd_marked(h, 0, A + 8, A, A, A, None, A, ws_need, A, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd_fp8_marked(h, A, A, A, A, A, A, None, A, ws_need, None, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd_fp8_marked(h, A, A, A, A, A, A, None, A, 16, A, None) == B.WFATTN_ERR_WORKSPACE
     # the gated forward
     G = L.wfattn_fwd_gated
     assert G(h, A, A, A, A, None, A, ws_need, None, A, 0, A, None) == B.WFATTN_ERR_NULL
