@@ -806,37 +806,70 @@ __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
 }
 
 // Merge of split key ranges: out = sum_k exp(lse_k - lse) * O_k, lse = log sum_k exp(lse_k).  One
-// thread per (row, 4 channels); a block covers 256 / (D/4) rows of one merge group.
+// thread per (row, 8 channels); a block covers 256 / (D/8) rows of one merge group.  The pieces are
+// taken in batches of kMergeBatch whose loads (lse and O alike) are all issued before any is used,
+// so a batch costs one memory round trip; a later batch rescales what the earlier ones summed to
+// its new running maximum.
+constexpr int kMergeBatch = 4;
+constexpr int kMergeTpr(int d) { return d / 8; }  // threads per row
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
-  constexpr int RPB = 256 / (D / 4);  // rows per block
+  constexpr int TPR = kMergeTpr(D), RPB = 256 / TPR;  // rows per block
   const int32_t* hdr = p.blob;
   if (ld_const(hdr, H_NONCE_LO) != (int32_t)p.nonce_lo || ld_const(hdr, H_NONCE_HI) != (int32_t)p.nonce_hi) return;
   const int grp = blockIdx.x / (BM / RPB), rblk = blockIdx.x % (BM / RPB);
   const int32_t* g = p.blob + ld_const(hdr, H_OFF_GROUPS) + (size_t)grp * kGroupInts;
   const int32_t* it = p.blob + ld_const(hdr, H_OFF_ITEMS) + (size_t)g[0] * kItemInts;
   const int head = it[0], q_row0 = it[1], rows = it[2], slot0 = g[1], parts = g[2];
-  const int r = rblk * RPB + threadIdx.x / (D / 4), d4 = threadIdx.x % (D / 4);
+  const int r = rblk * RPB + threadIdx.x / TPR, d8 = threadIdx.x % TPR;
   if (r >= rows) return;
-  float mx = -INFINITY;
-  for (int k = 0; k < parts; ++k) mx = fmaxf(mx, p.part_lse[(size_t)(slot0 + k) * BM + r]);
-  float z = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < parts; ++k) {
-    const float w = expf(p.part_lse[(size_t)(slot0 + k) * BM + r] - mx);
-    const float4 v = *reinterpret_cast<const float4*>(p.part_o + ((size_t)(slot0 + k) * BM + r) * D + 4 * d4);
-    z += w;
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+  float mx = -INFINITY, z = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < parts; k0 += kMergeBatch) {
+    float lk[kMergeBatch];
+    float4 ok[kMergeBatch][2];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      lk[j] = -INFINITY;
+      ok[j][0] = ok[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k0 + j < parts) {
+        const size_t row = (size_t)(slot0 + k0 + j) * BM + r;
+        lk[j] = p.part_lse[row];
+        const float4* src = reinterpret_cast<const float4*>(p.part_o + row * D + 8 * d8);
+        ok[j][0] = src[0];
+        ok[j][1] = src[1];
+      }
+    }
+    float mn = mx;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) mn = fmaxf(mn, lk[j]);
+    // every batch holds at least one piece with a finite lse, so mn is finite; exp(-inf) = 0
+    const float c = expf(mx - mn);
+    z *= c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= c;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = expf(lk[j] - mn);
+      z += w;
+      acc[0] += w * ok[j][0].x; acc[1] += w * ok[j][0].y; acc[2] += w * ok[j][0].z; acc[3] += w * ok[j][0].w;
+      acc[4] += w * ok[j][1].x; acc[5] += w * ok[j][1].y; acc[6] += w * ok[j][1].z; acc[7] += w * ok[j][1].w;
+    }
+    mx = mn;
   }
   const float iz = 1.f / z;
-  const size_t off = ((size_t)(q_row0 + r) * p.H + head) * D + 4 * d4;
+  const size_t off = ((size_t)(q_row0 + r) * p.H + head) * D + 8 * d8;
   if constexpr (OUT_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + off);
+    dst[0] = make_float4(acc[0] * iz, acc[1] * iz, acc[2] * iz, acc[3] * iz);
+    dst[1] = make_float4(acc[4] * iz, acc[5] * iz, acc[6] * iz, acc[7] * iz);
   } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
-        make_uint2(pack2_bf16(acc.x * iz, acc.y * iz), pack2_bf16(acc.z * iz, acc.w * iz));
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + off) =
+        make_uint4(pack2_bf16(acc[0] * iz, acc[1] * iz), pack2_bf16(acc[2] * iz, acc[3] * iz),
+                   pack2_bf16(acc[4] * iz, acc[5] * iz), pack2_bf16(acc[6] * iz, acc[7] * iz));
   }
-  if (p.lse && d4 == 0) p.lse[(size_t)head * p.lq + q_row0 + r] = mx + logf(z);
+  if (p.lse && d8 == 0) p.lse[(size_t)head * p.lq + q_row0 + r] = mx + logf(z);
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n4) {
@@ -871,7 +904,7 @@ hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream
 
 hipError_t launch_combine(const FwdParams& p, int head_dim, bool out_f32, int groups, hipStream_t s) {
   if (groups <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)groups * (BM / (256 / (head_dim / 4)));
+  const unsigned blocks = (unsigned)groups * (BM / (256 / kMergeTpr(head_dim)));
   if (head_dim == 128) {
     if (out_f32) hipLaunchKernelGGL((combine_kernel<128, true>), dim3(blocks), dim3(256), 0, s, p);
     else hipLaunchKernelGGL((combine_kernel<128, false>), dim3(blocks), dim3(256), 0, s, p);
