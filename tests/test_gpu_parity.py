@@ -80,6 +80,21 @@ def test_medium_all_elements(B, O, name, xcd):
     assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
 
 
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_merge_of_more_than_four_pieces(B, O, io):
+    """Items cut into up to 7 key ranges: the merge takes its pieces in batches of four, so the
+    second batch rescales what the first summed."""
+    c = medium_case("wave_round", seed=21)
+    if io == torch.float32:
+        c = type(c)(c.name, c.table, io, c.q.float(), c.k_pool.float(), c.v_pool.float())
+    print(f"[case] medium wave_round split_k=7 io={io}", flush=True)
+    out, lse, att = run(B, c, split_k=7)
+    assert int(att.plan.describe(0)[6]) > 4  # some item has more than four pieces
+    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    check_bf16(f64(out), ref, "wave_round split 7")
+    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+
+
 @pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])
 def test_full_size_sampled_rows(B, O, name):
     c = make_case(name)
