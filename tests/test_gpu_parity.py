@@ -130,6 +130,65 @@ def test_degenerate_tables(B, O):
             assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
 
 
+def _random_table(rng):
+    """A chunk table drawn at random: 1-6 chunks of 1-64, 65-300 or 301-500 tokens; a permutation
+    of orders, or (half the time) orders with ties; a random subset of query chunks in random
+    order; pages of 64-512 tokens, shuffled, with spare pages; 1-3 heads; head_dim 64 or 128; the
+    default or an explicit softmax scale."""
+    n = int(rng.integers(1, 7))
+    lo_hi = [(1, 65), (65, 301), (301, 501)]
+    tok = [int(rng.integers(*lo_hi[int(k)])) for k in rng.integers(0, 3, size=n)]
+    ties = bool(rng.integers(0, 2))
+    order = rng.integers(0, n, size=n) if ties else rng.permutation(n)
+    queries = rng.permutation(n)[:int(rng.integers(1, n + 1))]
+    page = int(rng.choice([64, 128, 256, 512]))
+    t = make_table(tok, order, queries, page, int(rng.integers(1, 4)), int(rng.choice([64, 128])),
+                   shuffle_rng=rng, spare=int(rng.integers(0, 3)), softmax_scale=float(rng.choice([0.0, 0.07])))
+    return t, ties
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_tables(B, O, seed):
+    """Seeded random tables through the bf16 forward (three ways of splitting keys), the e4m3
+    forward and the fp32-I/O forward, every element against the oracle.  Chunks that no query
+    chunk can see hold NaN K/V, so a read of any of them shows."""
+    rng = np.random.default_rng(1000 + seed)
+    t, ties = _random_table(rng)
+    c = fill_case("random", t, rng, torch.bfloat16)
+    top = max(int(t.chunk_order[a]) for a in t.query_chunks)
+    hidden = [b for b in range(t.num_chunks) if int(t.chunk_order[b]) > top]
+    _poison_chunks(c, hidden)
+    desc = (f"tokens={t.chunk_tokens.tolist()} order={t.chunk_order.tolist()} queries={t.query_chunks.tolist()} "
+            f"page={t.page_size} H={t.num_heads} d={t.head_dim} scale={t.softmax_scale} ties={ties}")
+    ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+    q, k, v = to_dev(c)
+    H, d = t.num_heads, t.head_dim
+    for split in (0, 1, 5):
+        print(f"[case] random seed={seed} bf16 split_k={split} {desc}", flush=True)
+        att = B.Attention(t, split_k=split, order_ties=int(ties))
+        out, lse = att.fwd(q, k, v, want_lse=True)
+        torch.cuda.synchronize()
+        check_bf16(f64(out), ref, desc)
+        assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    print(f"[case] random seed={seed} fp32 I/O {desc}", flush=True)
+    att = B.Attention(t, mode=B.WFATTN_WS_FP32, order_ties=int(ties))
+    out, lse = att.fwd(q.float(), k.float(), v.float(), want_lse=True)
+    torch.cuda.synchronize()
+    check_bf16(f64(out), ref, desc)
+    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    print(f"[case] random seed={seed} e4m3 {desc}", flush=True)
+    att8 = B.Attention(t, mode=B.WFATTN_WS_FP8, order_ties=int(ties))
+    rows = k.shape[0] * k.shape[1]
+    k8, ks = B.quantize_fp8(k.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(t, q)
+    out8, lse8 = att8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, want_lse=True)
+    torch.cuda.synchronize()
+    qdq, kdq = _dequantized_case(O, c)
+    ref_dq, ref_dq_lse = O.attn_rows(t, qdq, kdq, c.v_pool)
+    check_bf16(f64(out8), ref_dq, desc + " e4m3 (dequantized oracle)")
+    assert np.abs(f64(lse8).T - ref_dq_lse).max() <= LSE_TOL
+
+
 # ------------------------------------------------------------------ mask variants
 def _poison_chunks(c, chunks):
     """NaN into every pool slot of `chunks`: keys the mask must never read."""
