@@ -301,11 +301,12 @@ def _chunk_rows(c, b):
     return to(gk), to(gv)
 
 
-def test_publish_bit_exact(B, O):
+@pytest.mark.parametrize("d", [128, 64])
+def test_publish_bit_exact(B, O, d):
     """Every token of a chunk lands in its slot bit for bit as the oracle places it; no other slot
     (other chunks, padding) changes; the flag carries the generation."""
     rng = np.random.default_rng(51)
-    t = make_table([300, 129, 64, 700, 1], [2, 0, 1, 3, 4], [3], 256, 3, 128, shuffle_rng=rng, spare=2)
+    t = make_table([300, 129, 64, 700, 1], [2, 0, 1, 3, 4], [3], 256, 3, d, shuffle_rng=rng, spare=2)
     c = fill_case("pub", t, rng, torch.bfloat16)
     att = B.Attention(t)
     kp, vp = c.k_pool.clone().cuda(), c.v_pool.clone().cuda()
@@ -314,9 +315,9 @@ def test_publish_bit_exact(B, O):
     g = torch.Generator().manual_seed(3)
     for b in range(t.num_chunks):
         n = int(t.chunk_tokens[b])
-        sk = torch.randn(n, 3, 128, generator=g).to(torch.bfloat16)
-        sv = torch.randn(n, 3, 128, generator=g).to(torch.bfloat16)
-        print(f"[case] publish chunk {b} ({n} tokens)", flush=True)
+        sk = torch.randn(n, 3, d, generator=g).to(torch.bfloat16)
+        sv = torch.randn(n, 3, d, generator=g).to(torch.bfloat16)
+        print(f"[case] publish chunk {b} ({n} tokens, d={d})", flush=True)
         B.wfattn_publish_kv(att.plan, b, sk.cuda(), sv.cuda(), kp, vp, flags, 40 + b, att.ws)
         ref_k, ref_v = O.publish_kv(t, b, sk.view(torch.int16).numpy(), sv.view(torch.int16).numpy(), ref_k, ref_v)
     torch.cuda.synchronize()
@@ -646,12 +647,13 @@ def test_fp8_small_all_elements(B, O, name, split_k):
         check_fp8_contract(got, ref, name)
 
 
-def test_publish_fp8_bit_exact(B, O):
+@pytest.mark.parametrize("d", [128, 64])
+def test_publish_fp8_bit_exact(B, O, d):
     """e4m3 publish: per 64-token block of the chunk and head, the codes and the scale are the
     oracle quantizer's, placed in the chunk's pool rows and page-aligned scale blocks; V is copied
     bit for bit; nothing else in the pools changes."""
     rng = np.random.default_rng(61)
-    H, d = 3, 128
+    H = 3
     t = make_table([300, 129, 64, 1, 200], [1, 0, 2, 3, 4], [4], 256, H, d, shuffle_rng=rng, spare=2)
     att = B.Attention(t, mode=B.WFATTN_WS_FP8)
     rows = t.num_pages * t.page_size
@@ -668,7 +670,7 @@ def test_publish_fp8_bit_exact(B, O):
         sk = (torch.randn(n, H, d, generator=g) * (1 + b)).to(torch.bfloat16)
         sk[min(3, n - 1), 1, 7] = float("nan")  # a NaN is kept and ignored by the block amax
         sv = torch.randn(n, H, d, generator=g).to(torch.bfloat16)
-        print(f"[case] e4m3 publish chunk {b} ({n} tokens)", flush=True)
+        print(f"[case] e4m3 publish chunk {b} ({n} tokens, d={d})", flush=True)
         B.wfattn_publish_kv_fp8(att.plan, b, sk.cuda(), sv.cuda(), k8, ks, vp, flags, 9, att.ws)
         c8, csc = O.quantize_e4m3(sk)
         ref8, refv = O.publish_kv(t, b, c8, sv.view(torch.int16).numpy(), ref8, refv)
@@ -709,13 +711,14 @@ def test_publish_fp8_feeds_the_fp8_forward(B, O):
     assert torch.equal(out.cpu().view(torch.int16), out_ref.cpu().view(torch.int16))
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("k_e4m3", [False, True])
-def test_rope_publish_bit_exact(B, O, k_e4m3):
+def test_rope_publish_bit_exact(B, O, k_e4m3, d):
     """Fused pre-attention epilogue: rotated Q (bf16 and e4m3 with block scales), rotated K into
     the pages (bf16, or e4m3 with page-aligned scales), V into the pages -- each bit for bit what the
     oracle's rotation, bf16 rounding, quantizer and placement give; the flag carries the generation."""
     rng = np.random.default_rng(81)
-    H, d = 3, 128
+    H = 3
     t = make_table([130, 300, 64, 201], [0, 1, 2, 3], [3], 256, H, d, shuffle_rng=rng, spare=1)
     att = B.Attention(t, mode=B.WFATTN_WS_FP8 if k_e4m3 else B.WFATTN_WS_BF16)
     rows = t.num_pages * t.page_size
@@ -735,7 +738,7 @@ def test_rope_publish_bit_exact(B, O, k_e4m3):
             ks = torch.zeros((rows // 64, H), dtype=torch.float32, device="cuda")
         else:
             kp, k8, ks = torch.zeros_like(vp), None, None
-        print(f"[case] rope publish chunk {b} ({n} tokens) k_e4m3={k_e4m3}", flush=True)
+        print(f"[case] rope publish chunk {b} ({n} tokens) k_e4m3={k_e4m3} d={d}", flush=True)
         B.wfattn_rope_publish(att.plan, b, qkv.cuda(), cos_t.cuda(), sin_t.cuda(), q_out, q8, qs, kp, k8, ks, vp,
                               flags, 11, att.ws)
         torch.cuda.synchronize()
