@@ -240,6 +240,38 @@ def publish_and_gate(B, att, t, q, k, v, reps: int = 20):
                           "ungated_ms_same_run": round(float(np.median(times["plain"])), 4)}}
 
 
+def exp_peak_per_s(blocks: int = 2048, iters: int = 2048, reps: int = 5) -> float:
+    """v_exp_f32 the chip retires per second with nothing else running, measured by the probe
+    library built beside the attention library (8 workgroups of 256 lanes per CU, 8 independent
+    chains per lane); the best of `reps` event-timed launches."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "block_causal_chunk_amd", "libwfprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    L.wfprobe_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    L.wfprobe_exp_rate.restype = ctypes.c_int64
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    n = L.wfprobe_exp_rate(out.data_ptr(), blocks, iters, stream)  # warm-up
+    if n <= 0:
+        raise RuntimeError("wfprobe_exp_rate failed")
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.wfprobe_exp_rate(out.data_ptr(), blocks, iters, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, n / (e0.elapsed_time(e1) * 1e-3))
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("exp probe produced non-finite values")
+    return best
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """The oracle, as it stands, on a bounded sample of query rows of the same workload."""
     import numpy as np
@@ -398,6 +430,7 @@ def main():
     if not (f32 or args.no_extras):
         extra = publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v)
         extra.update(rope_publish(B, att, t, None if fp8 else k, k8 if fp8 else None, ks if fp8 else None, v))
+    exp_peak = exp_peak_per_s()
     ms = float(per.mean())
     attn_ms = float(per_attn.mean())
     flops = effective_flops(t)
@@ -449,6 +482,8 @@ def main():
                      "kernel_ms": round(attn_ms, 4), "merge_ms": round(ms - attn_ms, 4)},
         "mfma_counters": counters,
         "exps_per_s": round(exps / (ms * 1e-3), 1),
+        "exp_peak_per_s": round(exp_peak, 1),
+        "exp_frac": round(exps / (ms * 1e-3) / exp_peak, 4),
         "gather": gather,
         "wall_s_timed": round(wall, 3),
     }

@@ -1,4 +1,5 @@
-"""Build libwfattn.so in-tree with hipcc for gfx950 (runs on a host without a GPU)."""
+"""Build libwfattn.so (and the benchmark's probe, libwfprobe.so) in-tree with hipcc for gfx950
+(runs on a host without a GPU)."""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -13,6 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwfattn.so")
 SOURCES = ["plan.cpp", "api.hip", "attn_fwd.hip", "quant.hip", "publish.hip"]
+PROBE_LIB = os.path.join(HERE, "libwfprobe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -49,19 +52,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libwfattn.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n" + r.stdout)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libwfattn.so and libwfprobe.so (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

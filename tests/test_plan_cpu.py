@@ -33,6 +33,27 @@ def test_exports_every_declared_symbol(B):
         assert B.status_str(s) and B.status_str(s) != "unknown status"
 
 
+def test_probe_library_exports_and_rejects_bad_arguments(B):
+    """The benchmark's exp-rate probe: every symbol wfprobe.h declares is exported, and bad
+    arguments are refused before any HIP call."""
+    from block_causal_chunk_amd import build
+    path = build.PROBE_LIB
+    if not os.path.exists(path):
+        build.build()
+    hdr = open(os.path.join(ROOT, "include", "wfprobe.h")).read()
+    declared = set(re.findall(r"\b(wfprobe_[a-z0-9_]+)\s*\(", hdr))
+    L = ctypes.CDLL(path)
+    assert declared == {"wfprobe_exp_rate"}
+    for name in declared:
+        assert hasattr(L, name), name
+    L.wfprobe_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    L.wfprobe_exp_rate.restype = ctypes.c_int64
+    buf = (ctypes.c_float * 256)()
+    assert L.wfprobe_exp_rate(None, 1, 1, None) == -1
+    assert L.wfprobe_exp_rate(ctypes.addressof(buf), 0, 1, None) == -1
+    assert L.wfprobe_exp_rate(ctypes.addressof(buf), 1, 0, None) == -1
+
+
 def _plan_status(B, t, **opts):
     c, keep = B.make_table_c(t)
     o = B.OptsC(opts.get("split_k", 0), opts.get("xcd_remap", 0), opts.get("order_ties", 0), opts.get("r1", 0))
