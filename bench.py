@@ -272,8 +272,10 @@ def exp_peak_per_s(blocks: int = 2048, iters: int = 2048, reps: int = 5) -> floa
     return best
 
 
-def cpu_baseline(case, budget_s: float = 12.0):
-    """The oracle, as it stands, on a bounded sample of query rows of the same workload."""
+def cpu_baseline(case, budget_s: float = 15.0, min_s: float = 10.0):
+    """The oracle, as it stands, on a bounded sample of query rows of the same workload: the sample
+    grows until one timed run takes at least min_s seconds (aiming at budget_s), or covers every
+    row."""
     import numpy as np
 
     import oracle
@@ -290,9 +292,9 @@ def cpu_baseline(case, budget_s: float = 12.0):
         t0 = time.perf_counter()
         oracle.attn_rows(t, q, k, v, rows=rows)
         dt = time.perf_counter() - t0
-        if dt >= budget_s / 4 or n >= lq:
+        if dt >= min_s or n >= lq:
             break
-        n = min(lq, int(n * max(2.0, budget_s / max(dt, 1e-3) / 1.5)))
+        n = min(lq, int(n * min(8.0, max(1.2, budget_s / max(dt, 1e-3)))))
     # FLOPs of the sampled rows: each row sees the visible keys of its chunk
     qstart = np.concatenate([[0], np.cumsum([int(t.chunk_tokens[a]) for a in t.query_chunks])])
     vis = []
@@ -329,7 +331,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the publish and gated-forward measurements (profiling runs)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds the oracle sample aims at (at least 10)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (3 times) so that a "
                          "counter run can scale FETCH_SIZE/WRITE_SIZE against known bytes")
