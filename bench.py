@@ -337,7 +337,7 @@ def main():
                          "counter run can scale FETCH_SIZE/WRITE_SIZE against known bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (no collectives, no sharding); "
+        print("bench.py: the library runs on exactly one GPU (it has no collectives and no sharding); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
