@@ -92,6 +92,7 @@ def test_plan_errors(B):
     assert _plan_status(B, t) == B.WFATTN_ERR_INVALID
     assert mod(query_chunks=np.array([1, 1], np.int32)) == B.WFATTN_ERR_INVALID
     assert mod(query_chunks=np.array([3], np.int32)) == B.WFATTN_ERR_INVALID
+    assert mod(query_chunks=np.array([], np.int32)) == B.WFATTN_ERR_INVALID  # no query chunk
     assert mod(num_heads=0) == B.WFATTN_ERR_INVALID
     assert mod(softmax_scale=float("nan")) == B.WFATTN_ERR_INVALID
     t = _base()
