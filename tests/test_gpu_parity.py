@@ -396,6 +396,39 @@ def test_gate_skips_items_of_unpublished_chunks(B, O):
     check_bf16(f64(out), ref, "gate-open")
 
 
+@pytest.mark.parametrize("name", ["wan13b_task", "wave_round"])
+def test_full_size_publish_and_gate_are_bitwise(B, name):
+    """At full size, in the benchmark's launch configuration: pools rebuilt chunk by chunk with the
+    publish (from NaN) give the forward the same bits as the original pools, and the gated forward
+    with every chunk published returns the plain forward's bits and reports nothing."""
+    c = make_case(name)
+    t = c.table
+    q, k, v = to_dev(c)
+    att = B.Attention(t)
+    ref_out, ref_lse = att.fwd(q, k, v, want_lse=True)
+    kp = torch.full_like(k, float("nan"))
+    vp = torch.full_like(v, float("nan"))
+    flags = torch.zeros(t.num_chunks, dtype=torch.int32, device="cuda")
+    print(f"[case] full-size publish of every chunk, {name}", flush=True)
+    for b in range(t.num_chunks):
+        # chunk b's rows in token order, straight from the case's own pages
+        pages = torch.from_numpy(np.asarray(t.page_ids[t.page_offsets[b]:t.page_offsets[b + 1]], np.int64)).cuda()
+        n = int(t.chunk_tokens[b])
+        sk = k[pages].reshape(-1, t.num_heads, t.head_dim)[:n].contiguous()
+        sv = v[pages].reshape(-1, t.num_heads, t.head_dim)[:n].contiguous()
+        B.wfattn_publish_kv(att.plan, b, sk, sv, kp, vp, flags, 3, att.ws)
+    need = torch.full((t.num_chunks,), 3, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    print(f"[case] full-size gated forward over the published pools, {name}", flush=True)
+    B.wfattn_fwd_gated(att.plan, q, kp, vp, out, lse, att.ws, flags, need, 0, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse, ref_lse)
+
+
 def test_pool_beyond_4gib(B, O):
     """64-bit addressing: K and V pools of 8400 pages x 256 tokens x 8 heads x 128 bf16 (4.4 GB
     each), with every chunk's pages placed past the first 4 GiB.  The forward reads them and the
