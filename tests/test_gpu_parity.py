@@ -744,6 +744,35 @@ def test_publish_fp8_feeds_the_fp8_forward(B, O):
     assert torch.equal(out.cpu().view(torch.int16), out_ref.cpu().view(torch.int16))
 
 
+def test_full_size_publish_fp8_feeds_the_fp8_forward(B):
+    """wan14b_fp8 at full size (40 heads), in the benchmark's launch configuration: K8/scale and V
+    pools built chunk by chunk with the e4m3 publish give the e4m3 forward the bits it returns
+    over the whole pool quantized at once."""
+    c = make_case("wan14b_fp8")
+    t = c.table
+    H, d = t.num_heads, t.head_dim
+    q, k, v = to_dev(c)
+    rows = k.shape[0] * k.shape[1]
+    k8_ref, ks_ref = B.quantize_fp8(k.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(t, q)
+    att = B.Attention(t, mode=B.WFATTN_WS_FP8)
+    ref, ref_lse = att.fwd_fp8(q8, qs, k8_ref.view(k.shape), ks_ref, v, want_lse=True)
+    k8 = torch.zeros((rows, H, d), dtype=torch.uint8, device="cuda")
+    ks = torch.ones((rows // 64, H), dtype=torch.float32, device="cuda")
+    vp = torch.full_like(v, float("nan"))
+    print("[case] full-size e4m3 publish of every chunk, wan14b_fp8", flush=True)
+    for b in range(t.num_chunks):
+        pages = torch.from_numpy(np.asarray(t.page_ids[t.page_offsets[b]:t.page_offsets[b + 1]], np.int64)).cuda()
+        n = int(t.chunk_tokens[b])
+        sk = k[pages].reshape(-1, H, d)[:n].contiguous()
+        sv = v[pages].reshape(-1, H, d)[:n].contiguous()
+        B.wfattn_publish_kv_fp8(att.plan, b, sk, sv, k8, ks, vp, None, 0, att.ws)
+    out, lse = att.fwd_fp8(q8, qs, k8.view(k.shape), ks, vp, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(lse, ref_lse)
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("k_e4m3", [False, True])
 def test_rope_publish_bit_exact(B, O, k_e4m3, d):
