@@ -830,6 +830,62 @@ def test_rope_publish_bit_exact(B, O, k_e4m3, d):
     assert flags.cpu().tolist() == [0, 11, 0, 11]
 
 
+@pytest.mark.parametrize("k_e4m3", [False, True])
+def test_full_size_rope_publish_bit_exact(B, O, k_e4m3):
+    """The fused epilogue over one whole 4680-token chunk of the Wan-1.3B shape (12 heads, d 128):
+    rotated Q in bf16 and e4m3 with block scales, rotated K (bf16, or e4m3 with page-aligned
+    scales) and V in the chunk's pages, each bit for bit the oracle's."""
+    t = make_case("wan13b_task").table
+    H, d = t.num_heads, t.head_dim
+    rng = np.random.default_rng(91)
+    b = 3
+    n = int(t.chunk_tokens[b])
+    att = B.Attention(t, mode=B.WFATTN_WS_FP8 if k_e4m3 else B.WFATTN_WS_BF16)
+    rows = t.num_pages * t.page_size
+    qkv = torch.from_numpy(rng.standard_normal((n, 3, H, d)).astype(np.float32)).to(torch.bfloat16)
+    th = rng.uniform(-np.pi, np.pi, size=(n, d // 2))
+    cos_t = torch.from_numpy(np.cos(th).astype(np.float32))
+    sin_t = torch.from_numpy(np.sin(th).astype(np.float32))
+    q_out = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    q8 = torch.empty((n, H, d), dtype=torch.uint8, device="cuda")
+    qs = torch.empty(((n + 63) // 64, H), dtype=torch.float32, device="cuda")
+    vp = torch.zeros((t.num_pages, t.page_size, H, d), dtype=torch.bfloat16, device="cuda")
+    if k_e4m3:
+        kp, k8 = None, torch.zeros((rows, H, d), dtype=torch.uint8, device="cuda")
+        ks = torch.zeros((rows // 64, H), dtype=torch.float32, device="cuda")
+    else:
+        kp, k8, ks = torch.zeros_like(vp), None, None
+    flags = torch.zeros(t.num_chunks, dtype=torch.int32, device="cuda")
+    print(f"[case] full-size rope publish of chunk {b} ({n} tokens) k_e4m3={k_e4m3}", flush=True)
+    B.wfattn_rope_publish(att.plan, b, qkv.cuda(), cos_t.cuda(), sin_t.cuda(), q_out, q8, qs, kp, k8, ks, vp,
+                          flags, 4, att.ws)
+    torch.cuda.synchronize()
+    rq = torch.from_numpy(O.rotate_pairs(qkv[:, 0].float().numpy(), cos_t.numpy(), sin_t.numpy())).to(torch.bfloat16)
+    rk = torch.from_numpy(O.rotate_pairs(qkv[:, 1].float().numpy(), cos_t.numpy(), sin_t.numpy())).to(torch.bfloat16)
+    assert torch.equal(q_out.cpu().view(torch.int16), rq.view(torch.int16))
+    c8, csc = O.quantize_e4m3(rq)
+    assert np.array_equal(q8.cpu().numpy(), c8) and np.array_equal(qs.cpu().numpy(), csc)
+    zero16 = np.zeros((t.num_pages, t.page_size, H, d), np.int16)
+    v16 = qkv[:, 2].contiguous().view(torch.int16).numpy()
+    _, ref_v = O.publish_kv(t, b, v16, v16, zero16, zero16)
+    assert np.array_equal(vp.cpu().view(torch.int16).numpy(), ref_v)
+    if k_e4m3:
+        k8c, k8s = O.quantize_e4m3(rk)
+        z8 = np.zeros((t.num_pages, t.page_size, H, d), np.uint8)
+        ref8, _ = O.publish_kv(t, b, k8c, k8c, z8, z8)
+        assert np.array_equal(k8.cpu().numpy().reshape(ref8.shape), ref8)
+        refs = np.zeros((rows // 64, H), np.float32)
+        first = int(t.page_offsets[b])
+        for blk in range(k8s.shape[0]):
+            u = 64 * blk
+            refs[(int(t.page_ids[first + u // t.page_size]) * t.page_size + u % t.page_size) // 64] = k8s[blk]
+        assert np.array_equal(ks.cpu().numpy(), refs)
+    else:
+        ref_k, _ = O.publish_kv(t, b, rk.view(torch.int16).numpy(), rk.view(torch.int16).numpy(), zero16, zero16)
+        assert np.array_equal(kp.cpu().view(torch.int16).numpy(), ref_k)
+    assert flags.cpu().tolist() == [0, 0, 0, 4]
+
+
 def test_fp8_full_size_sampled_rows(B, O):
     c = make_case("wan14b_fp8")
     print("[case] fp8 full wan14b_fp8", flush=True)
