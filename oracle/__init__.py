@@ -6,8 +6,9 @@ import this package.  The product path (the HIP library and its binding) never d
 Two independent statements of the same definition live here:
   * ``wf_oracle.c`` (fp64, OpenMP): walks the page table chunk by chunk, two-pass softmax;
   * ``dense.py`` (numpy fp64): gathers keys, builds an explicit block-lower-triangular mask.
-plus an e4m3 codec and block quantizer written from the OCP 8-bit float definition, and the
-placement of a chunk's K/V into its pages (``publish_kv``).
+plus an e4m3 codec and block quantizer written from the OCP 8-bit float definition, the
+placement of a chunk's K/V into its pages (``publish_kv``) and the rotation of channel pairs
+(``rotate_pairs``).
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py``.
 """
 from __future__ import annotations
@@ -95,7 +96,11 @@ def max_threads() -> int:
 
 
 def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
-    """Attention of the query rows ``rows`` (default: all) of ``table``.
+    """Attention of the query rows ``rows`` (default: all) of ``table``: full inside a chunk,
+    block-causal across chunks (Wave Forcing project page, "01 - The design gap", directed
+    frontier and "Key observation"; KipQuest paper page, "The deep dive"), keys read from the
+    pages in place ("03 - End-to-end KV transport", panel "03 - Layout").  ``wf_oracle.c`` states
+    the rule and the two-pass softmax.
 
     q [Lq, H, d]; pools [num_pages, page_size, H, d]; any float dtype, widened to fp64 exactly.
     Returns (out [n, H, d], lse [n, H]) in fp64, natural log."""
@@ -139,7 +144,9 @@ def publish_kv(table, chunk: int, k_src, v_src, k_pool, v_pool):
 
 def rotate_pairs(x, cos_t, sin_t):
     """Rotary embedding of x [tokens, H, d] (any float; widened exactly to float32) by per-token,
-    per-pair angles given as cos_t, sin_t [tokens, d/2]: channel pair (2i, 2i+1) becomes
+    per-pair angles given as cos_t, sin_t [tokens, d/2].  The pages take Q and K as already
+    rotated and do not define the rotation; this is the usual rotary formula on adjacent channel
+    pairs, the reading the fused pre-attention epilogue implements: channel pair (2i, 2i+1) becomes
     (x0 c - x1 s, x0 s + x1 c).  Each product and each sum is one float32 operation (numpy
     float32 arithmetic rounds every operation to nearest-even; nothing is fused), so the result is
     the float32 value of that formula.  Returns float32 [tokens, H, d]."""
@@ -154,7 +161,9 @@ def rotate_pairs(x, cos_t, sin_t):
 
 
 def attn_masked(q, k, v, allowed, scale: float, nthreads: int = 0):
-    """One head, explicit mask: q [nq, d], k/v [nk, d], allowed [nq, nk] bool."""
+    """Softmax attention by its definition with an explicit 0/1 mask, one head: q [nq, d], k/v
+    [nk, d], allowed [nq, nk] bool.  The pins feed it masks built independently of the chunk
+    walk."""
     qd, kd, vd = _f64(q), _f64(k), _f64(v)
     al = np.ascontiguousarray(allowed, dtype=np.uint8)
     nq, d = qd.shape
@@ -170,19 +179,24 @@ def attn_masked(q, k, v, allowed, scale: float, nthreads: int = 0):
 
 
 def e4m3_decode(codes) -> np.ndarray:
+    """Value of each e4m3 code (OCP 8-bit floating point, E4M3FN), in fp64."""
     c = np.asarray(codes, dtype=np.uint8).ravel()
     L = lib()
     return np.array([L.oracle_e4m3_decode(int(x)) for x in c], dtype=np.float64).reshape(np.shape(codes))
 
 
 def e4m3_encode(x) -> np.ndarray:
+    """Nearest e4m3 code of each float32 value, ties to even, saturating to +-448, NaN kept."""
     a = np.asarray(x, dtype=np.float32).ravel()
     L = lib()
     return np.array([L.oracle_e4m3_encode(float(v)) for v in a], dtype=np.uint8).reshape(np.shape(x))
 
 
 def quantize_e4m3(x):
-    """x [rows, H, d] (bf16 values; any float dtype) -> (x8 uint8 [rows,H,d], scales f32 [ceil(rows/64),H])."""
+    """Block quantizer of the FP8 K/V transport (project page, "03 - End-to-end KV transport",
+    "Precision" panel), one fp32 scale per (64 consecutive rows, head): amax/448, codes = e4m3 of
+    x * (448/amax).  x [rows, H, d] (bf16 values; any float dtype) -> (x8 uint8 [rows,H,d],
+    scales f32 [ceil(rows/64),H])."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
@@ -200,6 +214,7 @@ def quantize_e4m3(x):
 
 
 def dequantize_e4m3(x8, scales) -> np.ndarray:
+    """decode(code) * scale of its (64-row block, head), in fp64: the values the e4m3 path means."""
     x8 = np.ascontiguousarray(x8, dtype=np.uint8)
     sc = np.ascontiguousarray(scales, dtype=np.float32)
     rows, H, d = x8.shape
@@ -211,7 +226,9 @@ def dequantize_e4m3(x8, scales) -> np.ndarray:
 
 
 def merge_lse(o_parts, lse_parts):
-    """o_parts [p, n, d], lse_parts [p, n] -> (out [n, d], lse [n])."""
+    """Softmax over a union of disjoint key sets from the parts' normalised outputs and LSEs:
+    out = sum_k exp(lse_k - lse) o_k, lse = log sum_k exp(lse_k) (an identity of the softmax; the
+    pages print no formula).  o_parts [p, n, d], lse_parts [p, n] -> (out [n, d], lse [n])."""
     o = _f64(o_parts)
     l = _f64(lse_parts)
     p, n, d = o.shape
