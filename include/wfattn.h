@@ -161,7 +161,9 @@ wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t what, int3
  * ws must hold wfattn_workspace_bytes(plan, dtype == WFATTN_FP32 ? WFATTN_WS_FP32 :
  * WFATTN_WS_BF16) bytes and have been filled by wfattn_plan_upload from this plan.  Device
  * pointers must be 16-byte aligned (ws 256-byte).  Padding slots of the pools are never read.
- * Concurrent calls on different streams need different workspaces.
+ * Concurrent calls on different streams need different workspaces.  The call only enqueues
+ * kernels (no allocation, copy, fill or synchronisation), so it may be captured in a HIP graph
+ * once the workspace has been uploaded.
  * Errors: NULL, INVALID, UNSUPPORTED, WORKSPACE, DEVICE. */
 wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
                          const void* k_pool, const void* v_pool, void* out, float* lse, void* ws,

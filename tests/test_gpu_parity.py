@@ -589,6 +589,46 @@ def test_marked_forwards_equal_unmarked(B):
     assert 0.0 <= t0.elapsed_time(mid) <= t0.elapsed_time(t1)
 
 
+def test_forwards_replay_from_a_hip_graph(B):
+    """The forwards only enqueue kernels (no allocation, copy, fill or synchronisation), so a caller
+    can capture them in a HIP graph: every replay, with eager work on the outputs in between,
+    returns the eager call's bits (split-K on, so the merge launch is captured too)."""
+    c = make_case("wan13b_task", small=True)
+    q, k, v = to_dev(c)
+    H, d = c.table.num_heads, c.table.head_dim
+    att = B.Attention(c.table, split_k=3)
+    ref, ref_lse = att.fwd(q, k, v, want_lse=True)
+    rows = k.shape[0] * k.shape[1]
+    k8, ks = B.quantize_fp8(k.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(c.table, q)
+    a8 = B.Attention(c.table, mode=B.WFATTN_WS_FP8, split_k=3)
+    ref8, ref8_lse = a8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, want_lse=True)
+    out, lse = torch.empty_like(ref), torch.empty_like(ref_lse)
+    out8, lse8 = torch.empty_like(ref8), torch.empty_like(ref8_lse)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one call on the capture stream before capturing
+        att.fwd(q, k, v, out=out, lse=lse)
+        a8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, out=out8, lse=lse8)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("[case] capture of the bf16 and e4m3 forwards", flush=True)
+    with torch.cuda.graph(g):
+        att.fwd(q, k, v, out=out, lse=lse)
+        a8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, out=out8, lse=lse8)
+    for i in range(3):
+        for x in (out, lse, out8, lse8):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        print(f"[case] graph replay {i}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
+        assert torch.equal(out8.view(torch.int16), ref8.view(torch.int16)) and torch.equal(lse8, ref8_lse)
+
+
 # ------------------------------------------------------------------ fp8
 def _quant_compare(O, x_cpu, codes_gpu, scales_gpu):
     ref8, ref_sc = O.quantize_e4m3(x_cpu)
