@@ -22,7 +22,7 @@ EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_work
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
             "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish", "wfattn_fwd_marked",
-            "wfattn_fwd_fp8_marked"]
+            "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 
 
@@ -84,6 +84,8 @@ def lib():
         L.wfattn_publish_kv.restype = i32
         L.wfattn_fwd_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, vp, vp]
         L.wfattn_fwd_gated.restype = i32
+        L.wfattn_fwd_fp8_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, vp, vp]
+        L.wfattn_fwd_fp8_gated.restype = i32
         L.wfattn_publish_kv_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
         L.wfattn_publish_kv_fp8.restype = i32
         L.wfattn_rope_publish.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz,
@@ -216,6 +218,14 @@ def wfattn_fwd_gated(plan: Plan, q, k_pool, v_pool, out, lse, ws, flags, need, s
     _check(lib().wfattn_fwd_gated(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(ws),
                                   ws.numel() * ws.element_size(), _ptr(flags), _ptr(need), int(spin_limit),
                                   _ptr(gate_status), _stream(stream)), "wfattn_fwd_gated")
+
+
+def wfattn_fwd_fp8_gated(plan: Plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, flags, need,
+                         spin_limit: int, gate_status, stream=None):
+    _check(lib().wfattn_fwd_fp8_gated(plan.handle, _ptr(q8), _ptr(q_scale), _ptr(k8_pool), _ptr(k_scale),
+                                      _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _ptr(flags), _ptr(need), int(spin_limit), _ptr(gate_status), _stream(stream)),
+           "wfattn_fwd_fp8_gated")
 
 
 def wfattn_fwd_marked(plan: Plan, dtype: int, q, k_pool, v_pool, out, lse, ws, attn_done_event: int, stream=None):

@@ -99,7 +99,7 @@ wfattn_status fwd_impl(const wfattn_plan_t* plan, wfattn_dtype dtype, const void
 
 wfattn_status fwd8_impl(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale, const uint8_t* k8_pool,
                         const float* k_scale, const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes,
-                        void* stream, hipEvent_t mark) {
+                        void* stream, const Gate* gate, hipEvent_t mark) {
   if (!plan || !q8 || !q_scale || !k8_pool || !k_scale || !v_pool || !out) return WFATTN_ERR_NULL;
   if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
   if (!ws) return WFATTN_ERR_WORKSPACE;
@@ -117,6 +117,12 @@ wfattn_status fwd8_impl(const wfattn_plan_t* plan, const uint8_t* q8, const floa
   fp.v = static_cast<const uint16_t*>(v_pool);
   fp.out = out;
   fp.lse = lse;
+  if (gate) {
+    fp.gate_flags = gate->flags;
+    fp.gate_need = gate->need;
+    fp.gate_status = gate->status;
+    fp.gate_spin = gate->spin;
+  }
   if (launch_attn_fp8(fp, P->head_dim, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (mark && hipEventRecord(mark, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (launch_combine(fp, P->head_dim, false, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
@@ -172,7 +178,19 @@ extern "C" wfattn_status wfattn_publish_kv(const wfattn_plan_t* plan, int32_t ch
 extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
                                         const uint8_t* k8_pool, const float* k_scale, const void* v_pool, void* out,
                                         float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, nullptr);
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" wfattn_status wfattn_fwd_fp8_gated(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                                              const uint8_t* k8_pool, const float* k_scale, const void* v_pool,
+                                              void* out, float* lse, void* ws, size_t ws_bytes,
+                                              const uint32_t* flags, const uint32_t* need, int32_t spin_limit,
+                                              uint32_t* gate_status, void* stream) {
+  if (!flags || !need || !gate_status) return WFATTN_ERR_NULL;
+  if (spin_limit < 0 || spin_limit > WFATTN_GATE_SPIN_MAX) return WFATTN_ERR_RANGE;
+  if (!aligned(flags, 4) || !aligned(need, 4) || !aligned(gate_status, 4)) return WFATTN_ERR_UNSUPPORTED;
+  const Gate g{flags, need, gate_status, spin_limit};
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, &g, nullptr);
 }
 
 extern "C" wfattn_status wfattn_fwd_marked(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
@@ -188,7 +206,7 @@ extern "C" wfattn_status wfattn_fwd_fp8_marked(const wfattn_plan_t* plan, const 
                                                void* out, float* lse, void* ws, size_t ws_bytes,
                                                void* attn_done_event, void* stream) {
   if (!attn_done_event) return WFATTN_ERR_NULL;
-  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream,
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, nullptr,
                    static_cast<hipEvent_t>(attn_done_event));
 }
 

@@ -18,8 +18,9 @@
 //   O^T += V^T . P^T    : P stays in registers as the B operand; V^T comes from LDS through
 //                         ds_read_b64_tr_b16 transposed reads; O lives in AGPRs
 //
-// Kernel instances: head_dim 64 / 128 x {bf16 out, fp32 out, e4m3 scores, gated bf16 out}; the
-// gated instance first checks, per item, the generation flags of the chunks it reads (gate_item).
+// Kernel instances: head_dim 64 / 128 x {bf16 out, fp32 out, e4m3 scores, gated bf16 out, gated
+// e4m3 scores}; a gated instance first checks, per item, the generation flags of the chunks it
+// reads (gate_item).
 //
 // The key loop is software-pipelined in half tiles (32 keys).  One half step issues the score
 // MFMAs of the next half and the P.V MFMAs of the previous half, one at a time, and between two
@@ -897,8 +898,13 @@ hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int 
 
 hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
+  if (head_dim == 128) {
+    if (p.gate_flags) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
+  } else {
+    if (p.gate_flags) hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -178,6 +178,17 @@ wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const
                              const uint8_t* k8_pool, const float* k_scale, const void* v_pool,
                              void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* wfattn_fwd_fp8 with the gate of wfattn_fwd_gated: the same flags, need, spin_limit and
+ * gate_status, with the same meaning and the same guarantees.
+ * Errors: as wfattn_fwd_fp8, plus NULL (flags, need, gate_status), RANGE (spin_limit < 0 or
+ * above WFATTN_GATE_SPIN_MAX). */
+wfattn_status wfattn_fwd_fp8_gated(const wfattn_plan_t* plan, const uint8_t* q8,
+                                   const float* q_scale, const uint8_t* k8_pool,
+                                   const float* k_scale, const void* v_pool, void* out, float* lse,
+                                   void* ws, size_t ws_bytes, const uint32_t* flags,
+                                   const uint32_t* need, int32_t spin_limit, uint32_t* gate_status,
+                                   void* stream);
+
 /* Measurement aid: wfattn_fwd and wfattn_fwd_fp8 with one more argument, a hipEvent_t (passed
  * as void*, created by the caller) that is recorded on `stream` between the attention launch and
  * the launch of the merge of split key ranges, so that the two can be timed apart with events.

@@ -26,7 +26,7 @@ def attn_asm(tmp_path_factory):
 
 def test_every_attention_kernel_is_hazard_free(attn_asm):
     names = re.findall(r"^(_Z\w*attn_fwd_kernel\w*):", attn_asm, re.M)
-    assert len(names) == 8, names  # {d64, d128} x {bf16 out, fp32 out, e4m3 scores, gated bf16 out}
+    assert len(names) == 10, names  # {d64, d128} x {bf16 out, fp32 out, e4m3 scores, gated bf16, gated e4m3}
     for n in names:
         found = check(kernel_body(attn_asm, n))
         assert not found, (n, found[:5])

@@ -429,6 +429,45 @@ def test_full_size_publish_and_gate_are_bitwise(B, name):
     assert torch.equal(lse, ref_lse)
 
 
+def test_gate_on_the_e4m3_forward(B):
+    """The gated e4m3 forward: with every flag ready it returns the ungated e4m3 forward's bits;
+    with the noisiest chunk one generation short (keys not split, so items are independent) its
+    query chunk's rows keep the caller's sentinel, the status bit is set, and every other row is
+    bit for bit the ungated result."""
+    c = medium_case("wave_round", seed=17)  # query chunks 2..6 of 7
+    t = c.table
+    H, d = t.num_heads, t.head_dim
+    q, k, v = to_dev(c)
+    rows = k.shape[0] * k.shape[1]
+    k8, ks = B.quantize_fp8(k.view(rows, H, d))
+    q8, qs = B.quantize_q_fp8(t, q)
+    att = B.Attention(t, mode=B.WFATTN_WS_FP8, split_k=1)
+    ref, ref_lse = att.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, want_lse=True)
+    n = t.num_chunks
+    need = torch.full((n,), 2, dtype=torch.int32, device="cuda")
+    flags = need.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full_like(ref, 7.0)
+    lse = torch.empty_like(ref_lse)
+    print("[case] gated e4m3 forward, every chunk ready", flush=True)
+    B.wfattn_fwd_fp8_gated(att.plan, q8, qs, k8.view(k.shape), ks, v, out, lse, att.ws, flags, need, 0, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
+    flags[6] = 1
+    out.fill_(7.0)
+    print("[case] gated e4m3 forward, chunk 6 one generation short, spin_limit 3", flush=True)
+    B.wfattn_fwd_fp8_gated(att.plan, q8, qs, k8.view(k.shape), ks, v, out, None, att.ws, flags, need, 3, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    qstart = np.concatenate([[0], np.cumsum([int(t.chunk_tokens[a]) for a in t.query_chunks])])
+    last = list(t.query_chunks).index(6)
+    r0, r1 = int(qstart[last]), int(qstart[last + 1])
+    assert (out[r0:r1] == 7.0).all()
+    assert torch.equal(out[:r0].view(torch.int16), ref[:r0].view(torch.int16))
+    assert torch.equal(out[r1:].view(torch.int16), ref[r1:].view(torch.int16))
+
+
 def test_pool_beyond_4gib(B, O):
     """64-bit addressing: K and V pools of 8400 pages x 256 tokens x 8 heads x 128 bf16 (4.4 GB
     each), with every chunk's pages placed past the first 4 GiB.  The forward reads them and the

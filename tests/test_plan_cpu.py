@@ -197,6 +197,15 @@ def test_call_errors_before_any_hip_call(B):
     assert G(h, A, A, A, A, None, A, ws_need, A + 2, A, 0, A, None) == B.WFATTN_ERR_UNSUPPORTED
     assert G(h, None, A, A, A, None, A, ws_need, A, A, 0, A, None) == B.WFATTN_ERR_NULL
     assert G(h, A, A, A, A, None, A, ws_need - 1, A, A, 0, A, None) == B.WFATTN_ERR_WORKSPACE
+    # the gated e4m3 forward
+    G8 = L.wfattn_fwd_fp8_gated
+    assert G8(h, A, A, A, A, A, A, None, A, ws_need, None, A, 0, A, None) == B.WFATTN_ERR_NULL
+    assert G8(h, A, A, A, A, A, A, None, A, ws_need, A, A, 0, None, None) == B.WFATTN_ERR_NULL
+    assert G8(h, A, A, A, A, A, A, None, A, ws_need, A, A, -1, A, None) == B.WFATTN_ERR_RANGE
+    assert G8(h, A, A, A, A, A, A, None, A, ws_need, A, A, B.WFATTN_GATE_SPIN_MAX + 1, A, None) == B.WFATTN_ERR_RANGE
+    assert G8(h, A, A, A, A, A, A, None, A, ws_need, A + 2, A, 0, A, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert G8(h, None, A, A, A, A, A, None, A, ws_need, A, A, 0, A, None) == B.WFATTN_ERR_NULL
+    assert G8(h, A, A, A, A, A, A, None, A, 16, A, A, 0, A, None) == B.WFATTN_ERR_WORKSPACE
     assert L.wfattn_quantize_fp8(A + 8, 10, 2, 128, A, A, None) == B.WFATTN_ERR_UNSUPPORTED
     assert L.wfattn_quantize_fp8(A, 0, 2, 128, A, A, None) == B.WFATTN_OK  # nothing to do, no launch
     assert L.wfattn_query_rows(None) == -1
