@@ -240,19 +240,32 @@ def publish_and_gate(B, att, t, q, k, v, reps: int = 20):
                           "ungated_ms_same_run": round(float(np.median(times["plain"])), 4)}}
 
 
+_PROBE = None
+
+
+def probe_lib():
+    """libwfprobe.so, the measurement probes built beside the attention library."""
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        path = os.path.join(ROOT, "block_causal_chunk_amd", "libwfprobe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(path)
+        L.wfprobe_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.wfprobe_exp_rate.restype = ctypes.c_int64
+        L.wfprobe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.wfprobe_copy.restype = ctypes.c_int32
+        _PROBE = L
+    return _PROBE
+
+
 def exp_peak_per_s(blocks: int = 2048, iters: int = 2048, reps: int = 5) -> float:
     """v_exp_f32 the chip retires per second with nothing else running, measured by the probe
     library built beside the attention library (8 workgroups of 256 lanes per CU, 8 independent
     chains per lane); the best of `reps` event-timed launches."""
-    import ctypes
-
     import torch
-    path = os.path.join(ROOT, "block_causal_chunk_amd", "libwfprobe.so")
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
-    L = ctypes.CDLL(path)
-    L.wfprobe_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
-    L.wfprobe_exp_rate.restype = ctypes.c_int64
+    L = probe_lib()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     n = L.wfprobe_exp_rate(out.data_ptr(), blocks, iters, stream)  # warm-up
@@ -333,7 +346,7 @@ def main():
                     help="skip the publish and gated-forward measurements (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds the oracle sample aims at (at least 10)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed steps, run a plain 256 MiB device copy (3 times) so that a "
+                    help="after the timed steps, run a plain 256 MiB copy kernel (3 times) so that a "
                          "counter run can scale FETCH_SIZE/WRITE_SIZE against known bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -420,11 +433,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if args.copy_calibration:
+        # the probe library's plain copy kernel, 256 MiB, so that a counter run can scale its
+        # memory counters by what they read for known bytes
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream().cuda_stream
         for _ in range(3):
-            dst.copy_(src)
+            if probe_lib().wfprobe_copy(dst.data_ptr(), src.data_ptr(), src.numel(), stream) != 0:
+                raise RuntimeError("wfprobe_copy failed")
         torch.cuda.synchronize()
+        if not bool(torch.equal(src, dst)):
+            raise RuntimeError("calibration copy is wrong")
         del src, dst
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
     per_attn = np.array([s.elapsed_time(m) for s, m in zip(starts, mids)])  # the attention kernel alone

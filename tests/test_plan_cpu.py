@@ -43,7 +43,7 @@ def test_probe_library_exports_and_rejects_bad_arguments(B):
     hdr = open(os.path.join(ROOT, "include", "wfprobe.h")).read()
     declared = set(re.findall(r"\b(wfprobe_[a-z0-9_]+)\s*\(", hdr))
     L = ctypes.CDLL(path)
-    assert declared == {"wfprobe_exp_rate"}
+    assert declared == {"wfprobe_exp_rate", "wfprobe_copy"}
     for name in declared:
         assert hasattr(L, name), name
     L.wfprobe_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
@@ -52,6 +52,14 @@ def test_probe_library_exports_and_rejects_bad_arguments(B):
     assert L.wfprobe_exp_rate(None, 1, 1, None) == -1
     assert L.wfprobe_exp_rate(ctypes.addressof(buf), 0, 1, None) == -1
     assert L.wfprobe_exp_rate(ctypes.addressof(buf), 1, 0, None) == -1
+    L.wfprobe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    L.wfprobe_copy.restype = ctypes.c_int32
+    a = ctypes.addressof(buf)
+    assert L.wfprobe_copy(None, a, 16, None) == -1
+    assert L.wfprobe_copy(a, None, 16, None) == -1
+    assert L.wfprobe_copy(a, a + 16 * 8, 0, None) == -1
+    assert L.wfprobe_copy(a, a + 16 * 8, 24, None) == -1
+    assert L.wfprobe_copy(a + 4, a + 16 * 8, 16, None) == -1
 
 
 def _plan_status(B, t, **opts):
