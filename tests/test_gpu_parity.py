@@ -978,3 +978,28 @@ def test_fp8_full_size_sampled_rows(B, O):
     qdq, kdq = _dequantized_case(O, c)
     ref_dq, _ = O.attn_rows(c.table, qdq, kdq, c.v_pool, rows=rows)
     check_bf16(got[rows], ref_dq, "wan14b_fp8 (dequantized oracle)")
+
+
+def test_measurement_probes():
+    """The benchmark's probes: the copy kernel copies exactly (an odd number of granules, a grid
+    capped below the size), and the exp-rate kernel's chains stay finite in [0.5, 1] per value."""
+    import ctypes
+    from block_causal_chunk_amd import build
+    L = ctypes.CDLL(build.PROBE_LIB)
+    L.wfprobe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    L.wfprobe_copy.restype = ctypes.c_int32
+    L.wfprobe_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    L.wfprobe_exp_rate.restype = ctypes.c_int64
+    stream = torch.cuda.current_stream().cuda_stream
+    n = 16 * (8192 * 256 * 3 + 5)  # more granules than one pass of the capped grid
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
+    print("[case] probe copy", flush=True)
+    assert L.wfprobe_copy(dst.data_ptr(), src.data_ptr(), n, stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src) and int(dst[n:].sum()) == 0
+    out = torch.empty(64 * 256, dtype=torch.float32, device="cuda")
+    print("[case] probe exp rate", flush=True)
+    assert L.wfprobe_exp_rate(out.data_ptr(), 64, 100, stream) == 64 * 256 * 8 * 100
+    torch.cuda.synchronize()
+    assert bool(((out >= 8 * 0.5) & (out <= 8.0)).all())
