@@ -143,6 +143,7 @@ extern "C" wfattn_status wfattn_fwd_gated(const wfattn_plan_t* plan, const void*
   if (!flags || !need || !gate_status) return WFATTN_ERR_NULL;
   if (spin_limit < 0 || spin_limit > WFATTN_GATE_SPIN_MAX) return WFATTN_ERR_RANGE;
   if (!aligned(flags, 4) || !aligned(need, 4) || !aligned(gate_status, 4)) return WFATTN_ERR_UNSUPPORTED;
+  if (!aligned(k_pool, 256) || !aligned(v_pool, 256)) return WFATTN_ERR_UNSUPPORTED;  // no line spans two pages
   const Gate g{flags, need, gate_status, spin_limit};
   return fwd_impl(plan, WFATTN_BF16, q, k_pool, v_pool, out, lse, ws, ws_bytes, stream, &g);
 }
@@ -189,6 +190,7 @@ extern "C" wfattn_status wfattn_fwd_fp8_gated(const wfattn_plan_t* plan, const u
   if (!flags || !need || !gate_status) return WFATTN_ERR_NULL;
   if (spin_limit < 0 || spin_limit > WFATTN_GATE_SPIN_MAX) return WFATTN_ERR_RANGE;
   if (!aligned(flags, 4) || !aligned(need, 4) || !aligned(gate_status, 4)) return WFATTN_ERR_UNSUPPORTED;
+  if (!aligned(k8_pool, 256) || !aligned(v_pool, 256)) return WFATTN_ERR_UNSUPPORTED;  // no line spans two pages
   const Gate g{flags, need, gate_status, spin_limit};
   return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, &g, nullptr);
 }
@@ -296,3 +298,4 @@ extern "C" wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, i
     return WFATTN_ERR_DEVICE;
   return WFATTN_OK;
 }
+

@@ -501,14 +501,41 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   struct Desc {
     int row0, nv;
   };
+  // Past the segment's end a descriptor repeats the segment's last tile: the constant-count fills
+  // of the last steps then re-read keys this item is already reading, never a page of a chunk
+  // outside its visible prefix (in gated kernels: never one whose flag it has not seen).
   auto load_desc = [&](int j) -> Desc {
-    if (j >= n) return Desc{0, BN};  // past the segment: never used for a fill
-    const int t = tix(j);
+    const int t = tix(j < n ? j : n - 1);
     return Desc{ld_const(tiles, t), ld_const(tiles, t + 1)};
   };
-  auto k_scale_of = [&](const Desc& d) -> float {
-    if constexpr (FP8) return ld_const(p.k_scale, (d.row0 / 64) * H + head);
-    else return 1.f;
+  // e4m3 key-block scale of the segment's tile j (one scale per 64-key tile and head: tiles
+  // never cross a page and pages hold a multiple of 64 keys).  Ungated kernels read it through
+  // the scalar cache, which is right for memory that no one writes during the launch.  In gated
+  // kernels a producer may write the scales while the launch runs, so they are read like the
+  // flags, with device-coherent vector loads: 64 tiles' scales at once, one per lane, each
+  // 64-tile batch loaded when the walk first needs it, and picked out of the batch with a
+  // readlane (a reload costs one vmcnt wait per 64 tiles).
+  float sbatch = 1.f;
+  int sb_cur = -1;
+  auto coherent_scale = [&](int jt) -> float {
+    const int row0 = tiles[tix(jt)];
+    return __hip_atomic_load(p.k_scale + (size_t)(row0 / 64) * H + head, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto k_scale_of = [&](int j, const Desc& d) -> float {
+    if constexpr (FP8 && GATED) {
+      const int jt = j < n ? j : n - 1;
+      const int b = jt >> 6;
+      if (b != sb_cur) {
+        const int jl = 64 * b + (threadIdx.x & 63);
+        sbatch = jl < n ? coherent_scale(jl) : 1.f;
+        sb_cur = b;
+      }
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbatch), jt & 63));
+    } else if constexpr (FP8) {
+      return ld_const(p.k_scale, (d.row0 / 64) * H + head);
+    } else {
+      return 1.f;
+    }
   };
   // slot s: K of tile s+1 (descriptor dk) and V of tile s (descriptor dv), into buffer B
   auto fill_slot = [&](auto bufc, int s, const Desc& dk, const Desc& dv) {
@@ -550,8 +577,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     f32x16 s_a[2];      // scores of the current tile's second half
     bf16x8 p_a[2][2];   // P of the current tile's first half
     float cm_cur[2];
-    set_cm(k_scale_of(d0), cm_cur);
-    float ksc_nxt = k_scale_of(d1);
+    set_cm(k_scale_of(0, d0), cm_cur);
+    float ksc_nxt = k_scale_of(1, d1);
     int nv_cur = d0.nv;
     if (wave_active) {
       f32x16 s0[2];
@@ -575,7 +602,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       d3.nv = __builtin_amdgcn_readfirstlane(d3.nv);
       asm volatile("" : "+s"(d3.row0), "+s"(d3.nv));
       // slot j+2 (K of tile j+3, V of tile j+2) is filled from inside the two half steps; past
-      // the segment's end the descriptors point at pool row 0, so every step issues the same
+      // the segment's end the descriptors repeat its last tile, so every step issues the same
       // number of (in-bounds) loads and the wait below is a constant
       constexpr int FB = (B + 2) % NBUF;
       const bool k_ragged = d3.nv < BN, v_ragged = d2.nv < BN;  // rare: a chunk's last tile
@@ -587,7 +614,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       const uint32_t fvl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[FB] + ld.wave_u * VI * 1024;
       // descriptors for the next step
       const Desc d4 = load_desc(j + 4);
-      const float ksc_n2 = k_scale_of(d2);
+      const float ksc_n2 = k_scale_of(j + 2, d2);
       const int nv_nxt = d1.nv;
       float cm_nxt[2];
       set_cm(ksc_nxt, cm_nxt);
@@ -684,7 +711,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       __syncthreads();
       if (wave_active) {
         float cm[2];
-        set_cm(k_scale_of(dj), cm);
+        set_cm(k_scale_of(j, dj), cm);
         f32x16 s0[2], s1[2];
         scores_tile(reinterpret_cast<const uint8_t*>(smem_k[0]), dj.nv, s0, s1);
 #pragma unroll
@@ -745,12 +772,17 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
 // the wait always ends) and the decision is shared through LDS, so the whole workgroup takes the
 // same branch.  A chunk that is not ready skips the item and sets bit 0 of the caller's status.
 //
-// Memory ordering.  The flags are read with device-coherent (agent-scope) atomic loads.  No key or
-// value of a chunk is read in this kernel before its flag is seen (every item of every workgroup
-// passes this gate first), and the caches hold nothing of this kernel's from before its start, so
-// a chunk's pages cannot be stale in any cache once its flag is up.  An agent-scope acquire would
-// invalidate this XCD's L2 at every item and throw away the K/V reuse between the workgroups that
-// share it; it is issued only after a poll that had to wait for a producer running alongside.
+// Memory ordering.  The flags are read with device-coherent (agent-scope) relaxed atomic loads.
+// No key or value of a chunk is read in this kernel before its flag is seen: every item of every
+// workgroup passes this gate first, an item's tile fills (those past a segment's end included)
+// only touch the tiles of its visible prefix, and the entry points require pools aligned to 256
+// bytes, so with pages a multiple of 4 KB long no cache line holds bytes of two pages.  The
+// caches hold nothing of this kernel's from before its start, so a chunk's pages cannot be stale
+// in any cache once its flag is up.  The e4m3 key scales pack several pages' blocks into one
+// line, so gated kernels read them with the same coherent loads as the flags (k_scale_of).  An
+// agent-scope acquire would invalidate this XCD's L2 at every item and throw away the K/V reuse
+// between the workgroups that share it; it is issued only after a poll that had to wait for a
+// producer running alongside.
 __device__ bool gate_item(const FwdParams& p, const int32_t* items, int item, int* decision) {
   const int32_t* byrank = p.blob + ld_const(p.blob, H_OFF_BYRANK);
   const int last = ld_const(items, item * kItemInts + 6);

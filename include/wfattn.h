@@ -179,9 +179,11 @@ wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const
                              void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* wfattn_fwd_fp8 with the gate of wfattn_fwd_gated: the same flags, need, spin_limit and
- * gate_status, with the same meaning and the same guarantees.
+ * gate_status, with the same meaning and the same guarantees (k8_pool and v_pool 256-byte
+ * aligned).  The key scales are read with the same device-coherent loads as the flags, so a
+ * producer may write them while the call runs.
  * Errors: as wfattn_fwd_fp8, plus NULL (flags, need, gate_status), RANGE (spin_limit < 0 or
- * above WFATTN_GATE_SPIN_MAX). */
+ * above WFATTN_GATE_SPIN_MAX), UNSUPPORTED (pools not 256-byte aligned). */
 wfattn_status wfattn_fwd_fp8_gated(const wfattn_plan_t* plan, const uint8_t* q8,
                                    const float* q_scale, const uint8_t* k8_pool,
                                    const float* k_scale, const void* v_pool, void* out, float* lse,
@@ -275,13 +277,16 @@ wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t chunk, cons
 
 /* wfattn_fwd (bf16 I/O) with a gate: before a work item reads any key, every chunk b it sees must
  * have flags[b] >= need[b] (uint32 device arrays [num_chunks]).  The item's first wave polls the
- * flags with acquire loads at most spin_limit + 1 times (0: check once, never wait), sleeping
- * between polls; if they are still short, the item is skipped and bit 0 of *gate_status (device,
- * set with an atomic OR, never cleared by the library) is set.  Rows of skipped items, and of
- * items merged with them, are then unspecified; every other row is exact.  A wait never
- * deadlocks: it ends after spin_limit polls even if no producer ever runs.
+ * flags with device-coherent relaxed loads at most spin_limit + 1 times (0: check once, never
+ * wait), sleeping between polls; if a poll had to wait, an acquire fence at device scope follows
+ * the successful one.  If the flags are still short, the item is skipped and bit 0 of
+ * *gate_status (device, set with an atomic OR, never cleared by the library) is set.  Rows of
+ * skipped items, and of items merged with them, are then unspecified; every other row is exact.
+ * No page of a chunk is read before its flag has been seen, so k_pool and v_pool must be 256-byte
+ * aligned (then no cache line holds bytes of two pages).  A wait never deadlocks: it ends after
+ * spin_limit polls even if no producer ever runs.
  * Errors: as wfattn_fwd, plus NULL (flags, need, gate_status), RANGE (spin_limit < 0 or above
- * WFATTN_GATE_SPIN_MAX). */
+ * WFATTN_GATE_SPIN_MAX), UNSUPPORTED (pools not 256-byte aligned). */
 wfattn_status wfattn_fwd_gated(const wfattn_plan_t* plan, const void* q, const void* k_pool,
                                const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes,
                                const uint32_t* flags, const uint32_t* need, int32_t spin_limit,
