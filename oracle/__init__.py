@@ -54,7 +54,7 @@ def lib():
         L.oracle_attn_rows.argtypes = [ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_double, _f64p, _f64p, _f64p,
-                                       ctypes.c_int64, _i64p, _f64p, _f64p, ctypes.c_int32]
+                                       ctypes.c_int64, _i64p, _f64p, _f64p, _f64p, ctypes.c_int32]
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -95,7 +95,7 @@ def max_threads() -> int:
     return int(lib().oracle_max_threads())
 
 
-def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
+def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0, want_sumw2: bool = False):
     """Attention of the query rows ``rows`` (default: all) of ``table``: full inside a chunk,
     block-causal across chunks (Wave Forcing project page, "01 - The design gap", directed
     frontier and "Key observation"; KipQuest paper page, "The deep dive"), keys read from the
@@ -103,7 +103,9 @@ def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
     the rule and the two-pass softmax.
 
     q [Lq, H, d]; pools [num_pages, page_size, H, d]; any float dtype, widened to fp64 exactly.
-    Returns (out [n, H, d], lse [n, H]) in fp64, natural log."""
+    Returns (out [n, H, d], lse [n, H]) in fp64, natural log; with ``want_sumw2`` also
+    sumw2 [n, H], the sum of the squared softmax weights of each row (no part of the attention:
+    the tests size the LSE's rounding spread with it)."""
     H, d = int(table.num_heads), int(table.head_dim)
     qd, kd, vd = _f64(q), _f64(k_pool), _f64(v_pool)
     lq = int(sum(int(table.chunk_tokens[c]) for c in table.query_chunks))
@@ -112,6 +114,7 @@ def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
     rows = np.arange(lq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
     out = np.empty((rows.shape[0], H, d), np.float64)
     lse = np.empty((rows.shape[0], H), np.float64)
+    w2 = np.empty((rows.shape[0], H), np.float64) if want_sumw2 else None
     ints = [np.ascontiguousarray(a, np.int32) for a in (table.chunk_tokens, table.chunk_order,
                                                         table.page_offsets, table.page_ids,
                                                         table.query_chunks)]
@@ -120,10 +123,10 @@ def attn_rows(table, q, k_pool, v_pool, rows=None, nthreads: int = 0):
                                 int(table.page_size), len(ints[4]), _p(ints[4], _i32p), H, d,
                                 resolve_scale(table), _p(qd, _f64p), _p(kd, _f64p), _p(vd, _f64p),
                                 rows.shape[0], _p(rows, _i64p), _p(out, _f64p), _p(lse, _f64p),
-                                int(nthreads))
+                                None if w2 is None else _p(w2, _f64p), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_rows failed with code %d" % rc)
-    return out, lse
+    return (out, lse, w2) if want_sumw2 else (out, lse)
 
 
 def publish_kv(table, chunk: int, k_src, v_src, k_pool, v_pool):

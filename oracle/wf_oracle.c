@@ -104,13 +104,16 @@ int oracle_attn_masked(int64_t nq, int64_t nk, int32_t d, double scale, const do
 /* u % page_size.  Pools are [num_pages, page_size, H, d]; q is [Lq, H, d] where the query rows */
 /* are the tokens of query_chunks[0], query_chunks[1], ... concatenated.                        */
 /* rows[n_rows] lists the query rows to evaluate; out is [n_rows, H, d], lse is [n_rows, H].    */
+/* sumw2 (NULL: not computed) is [n_rows, H]: the sum over visible keys of the squared softmax  */
+/* weights, sum_j (exp(s_j - m) / Z)^2.  It is no part of the attention; the tests use it to    */
+/* size the spread that rounding each weight before the normaliser is summed leaves in an LSE.  */
 /* ------------------------------------------------------------------------------------------ */
 int oracle_attn_rows(int32_t num_chunks, const int32_t* chunk_tokens, const int32_t* chunk_order,
                      const int32_t* page_offsets, const int32_t* page_ids, int32_t num_pages,
                      int32_t page_size, int32_t num_query_chunks, const int32_t* query_chunks,
                      int32_t H, int32_t d, double scale, const double* q, const double* k_pool,
                      const double* v_pool, int64_t n_rows, const int64_t* rows, double* out,
-                     double* lse, int32_t nthreads) {
+                     double* lse, double* sumw2, int32_t nthreads) {
   if (num_chunks < 1 || !chunk_tokens || !chunk_order || !page_offsets || !page_ids ||
       num_pages < 1 || page_size < 1 || num_query_chunks < 1 || !query_chunks || H < 1 || d < 1 ||
       !q || !k_pool || !v_pool || n_rows < 0 || (n_rows > 0 && (!rows || !out || !lse)))
@@ -176,11 +179,14 @@ int oracle_attn_rows(int32_t num_chunks, const int32_t* chunk_tokens, const int3
         for (int64_t j = 0; j < n; ++j) z += exp(s[j] - m);
         double* o = out + (r * H + h) * (int64_t)d;
         for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+        double w2 = 0.0;
         for (int64_t j = 0; j < n; ++j) {
           const double p = exp(s[j] - m) / z;
           for (int32_t c = 0; c < d; ++c) o[c] += p * vrow[j][c];
+          w2 += p * p;
         }
         lse[r * H + h] = m + log(z);
+        if (sumw2) sumw2[r * H + h] = w2;
       }
     }
     free(s);

@@ -13,16 +13,29 @@ Gates (applied to the whole compared tensor, in fp64, against the oracle):
                   rounding alone gives a mean of about 1.1e-3*rms, so the mean gate leaves ~2x
                   headroom and still fails a kernel that drops one chunk's 72 tail keys
                   (mean ~4.6e-2*rms).
-  lse           : |err| <= LSE_TOL = 4e-3 (natural log).  The row sum is taken over the
-                  bf16-rounded P, each within a factor 1 +- 2^-8 of the exact weight, so the
-                  sum -- and exp(lse) -- is within that factor: |err| <= ln(1 + 2^-8) ~ 3.9e-3.
+  lse           : check_lse.  The kernel's row sum l is taken over the bf16-rounded weights
+                  P_j (fp32 sums), so lse = m + log(l) carries e = log(sum (P_j + d_j) / sum P_j)
+                  ~ sum_j d_j / sum_j P_j, where d_j is the rounding error of P_j.  Worst case
+                  |d_j| <= u P_j (u = 2^-8, bf16's unit roundoff), so |e| <= ln(1 + u) ~ 3.9e-3
+                  for every row: that is the per-row cap.  Round-to-nearest-even of a value
+                  spread over a binade leaves d_j zero-mean with variance at most (u P_j)^2 / 3,
+                  independent across j, so e has a standard deviation of at most
+                  sigma = (u / sqrt 3) sqrt(sum_j w_j^2), w_j = P_j / sum P the softmax weights
+                  (the oracle returns sum_j w_j^2).  fp32 arithmetic on m and log(l) adds
+                  ~2^-23 |lse|.  Gate: mean over rows of |e| / sigma' <= 1.5 and max <= 8, with
+                  sigma' = sqrt(sigma^2 + (1e-6 + 2^-22 |lse|)^2).  A simulation of this
+                  rounding on N(0,1) rows gives a mean ratio of 0.5-0.65 and a max of ~2.6 over
+                  200 rows; a kernel that drops one chunk's 72 tail keys at 18,720 keys shifts
+                  every row of that chunk by ~3.85e-3 -- under the per-row cap -- and gives a
+                  mean ratio of ~140, so the mean gate fails it.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-LSE_TOL = 4e-3
+U_BF16 = 2.0 ** -8
+LSE_CAP = float(np.log1p(U_BF16))  # worst case of any single row (see the module docstring)
 
 
 def stats(out, ref):
@@ -35,10 +48,15 @@ def stats(out, ref):
                 nmax=float(err.max()) / rms, nmean=float(err.mean()) / rms)
 
 
-def check_bf16(out, ref, what=""):
+def check_bf16(out, ref, what="", contract=True):
+    """The bf16 gates.  contract=False keeps only the self gates, for inputs whose outputs are not
+    the configs' small-scale ones: a row dominated by one key passes that key's V row through,
+    unit-scale, and rounding such an output to bf16 alone may cost 2^-8 |o| (1.4e-2 at |o| = 3.5),
+    above the contract's absolute 1e-2; the relative self gates still bound it."""
     s = stats(out, ref)
     assert np.isfinite(out).all(), what
-    assert s["max"] <= 1e-2 and s["mean"] <= 1e-3, (what, "contract", s)
+    if contract:
+        assert s["max"] <= 1e-2 and s["mean"] <= 1e-3, (what, "contract", s)
     assert s["nmean"] <= 2e-3 and s["cos"] >= 0.99999, (what, "self", s)
     err = np.abs(np.asarray(out, np.float64) - np.asarray(ref, np.float64))
     bound = 2.0 ** -7 * np.abs(ref) + 3e-2 * s["rms"]
@@ -69,10 +87,36 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def sample_rows(lq, block_m=128, n=40, seed=0):
-    """Rows spread over the query tiles, plus tile edges and the ragged tail."""
+def sample_rows(lq, block_m=256, n=40, seed=0):
+    """Rows spread over the query tiles, plus the edges of the kernel's 256-row query tiles and
+    of its 64-row waves, and the ragged tail."""
     rng = np.random.default_rng(seed)
-    edge = [0, 1, block_m - 1, block_m, lq - 1, lq - 2, (lq // block_m) * block_m, lq // 2]
+    edge = [0, 1, 63, 64, block_m - 1, block_m, 2 * block_m - 1, 2 * block_m, lq - 1, lq - 2,
+            (lq // block_m) * block_m, (lq // block_m) * block_m - 1, lq // 2]
     rows = set(int(r) for r in edge if 0 <= r < lq)
     rows.update(int(r) for r in rng.choice(lq, size=min(n, lq), replace=False))
     return np.array(sorted(rows), np.int64)
+
+
+def lse_ratios(got, ref, sumw2):
+    """|got - ref| / sigma' per row (see the module docstring); all arrays [n, H]."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    w2 = np.asarray(sumw2, np.float64)
+    assert got.shape == ref.shape == w2.shape, (got.shape, ref.shape, w2.shape)
+    sig = np.sqrt((U_BF16 ** 2 / 3.0) * w2 + (1e-6 + 2.0 ** -22 * np.abs(ref)) ** 2)
+    return np.abs(got - ref), np.abs(got - ref) / sig
+
+
+def check_lse(got, ref, sumw2, what=""):
+    """LSE gate: every row within the worst-case cap ln(1 + 2^-8) (plus the fp32 floor), and the
+    rounding spread over all rows within what rounding each weight to bf16 can leave."""
+    err, r = lse_ratios(got, ref, sumw2)
+    assert np.isfinite(np.asarray(got, np.float64)).all(), what
+    cap = LSE_CAP + 1e-6 + 2.0 ** -22 * np.abs(np.asarray(ref, np.float64))
+    assert (err <= cap).all(), (what, "lse cap", float(err.max()))
+    # the mean is a statistic of many rows: with fewer than 64 (row, head) pairs only the cap and
+    # the max hold (one dominant key gives a ratio of up to sqrt(3) on its own)
+    assert r.size < 64 or float(r.mean()) <= 1.5, (what, "lse spread (mean)", float(r.mean()), float(r.max()))
+    assert float(r.max()) <= 8.0, (what, "lse spread (max)", float(r.mean()), float(r.max()))
+    return float(r.mean()), float(r.max())

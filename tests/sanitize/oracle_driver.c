@@ -12,7 +12,7 @@ int oracle_attn_rows(int32_t num_chunks, const int32_t* chunk_tokens, const int3
                      int32_t page_size, int32_t num_query_chunks, const int32_t* query_chunks,
                      int32_t H, int32_t d, double scale, const double* q, const double* k_pool,
                      const double* v_pool, int64_t n_rows, const int64_t* rows, double* out,
-                     double* lse, int32_t nthreads);
+                     double* lse, double* sumw2, int32_t nthreads);
 int oracle_attn_masked(int64_t nq, int64_t nk, int32_t d, double scale, const double* q,
                        const double* k, const double* v, const uint8_t* allowed, double* out,
                        double* lse, int32_t nthreads);
@@ -54,10 +54,12 @@ int main(void) {
     for (int64_t r = 0; r < lq; ++r) rows[r] = r;
     double* out = malloc(sizeof(double) * (size_t)lq * H * d);
     double* lse = malloc(sizeof(double) * (size_t)lq * H);
+    double* w2 = malloc(sizeof(double) * (size_t)lq * H);
     if (oracle_attn_rows(n, tokens, order, offs, ids, npages, page, nq, q, H, d, 0.0, qq, kp, vp, lq, rows,
-                         out, lse, 2) != 0) { printf("attn_rows\n"); return 1; }
+                         out, lse, w2, 2) != 0) { printf("attn_rows\n"); return 1; }
+    for (size_t i = 0; i < (size_t)lq * H; ++i) if (!(w2[i] > 0.0 && w2[i] <= 1.0)) { printf("sumw2\n"); return 1; }
     for (size_t i = 0; i < (size_t)lq * H * d; ++i) if (!isfinite(out[i])) { printf("nonfinite\n"); return 1; }
-    free(ids); free(kp); free(vp); free(qq); free(rows); free(out); free(lse);
+    free(ids); free(kp); free(vp); free(qq); free(rows); free(out); free(lse); free(w2);
   }
   {  /* explicit mask, one head */
     enum { NQ = 37, NK = 53, D = 16 };

@@ -467,6 +467,54 @@ def test_p9_merging_key_partitions(oracle_lib):
     assert np.abs(mo - full_o).max() <= 1e-13 and np.abs(ml - full_l).max() <= 1e-13
 
 
+def test_p9_masked_form_against_sdpa_float64(oracle_lib):
+    """The explicit-mask form the merge pin leans on, against torch's float64 SDPA and logsumexp
+    with arbitrary boolean masks (not block-shaped), an explicit scale and the default 1/sqrt(d);
+    a row with no visible key is NaN with lse -inf."""
+    rng = np.random.default_rng(19)
+    for nq, nk, d, scale in [(23, 61, 32, 0.2), (40, 17, 64, 1 / 8), (9, 130, 16, 0.25)]:
+        q, k, v = (rng.standard_normal(s) for s in [(nq, d), (nk, d), (nk, d)])
+        allowed = rng.random((nq, nk)) < 0.4
+        allowed[np.arange(nq), rng.integers(0, nk, size=nq)] = True
+        o, l = oracle_lib.attn_masked(q, k, v, allowed, scale)
+        qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+        m = torch.from_numpy(allowed)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], attn_mask=m[None],
+                                                               scale=scale)[0]
+        assert np.abs(o - ref.numpy()).max() <= 1e-12
+        sc = (qt @ kt.T * scale).masked_fill(~m, float("-inf"))
+        assert np.abs(l - torch.logsumexp(sc, dim=-1).numpy()).max() <= 1e-12
+    allowed = np.ones((3, 5), bool)
+    allowed[1] = False
+    q, k, v = (rng.standard_normal(s) for s in [(3, 8), (5, 8), (5, 8)])
+    o, l = oracle_lib.attn_masked(q, k, v, allowed, 0.5)
+    assert np.isnan(o[1]).all() and l[1] == -np.inf and np.isfinite(o[[0, 2]]).all()
+
+
+def test_sum_of_squared_weights(oracle_lib):
+    """The oracle's sum_j w_j^2 (used to size the LSE rounding gate): against torch's float64
+    softmax of the masked scores; 1/N for a zero query (equal weights over N visible keys); 1 for
+    a single visible key."""
+    rng = np.random.default_rng(23)
+    tokens, order, queries, H, d = [11, 7, 19], [1, 0, 2], [0, 2, 1], 2, 16
+    c = _contiguous_case(rng, tokens, order, queries, H, d)
+    _, _, w2 = oracle_lib.attn_rows(c.table, c.q, c.k_pool, c.v_pool, want_sumw2=True)
+    keys = c.k_pool.double()[:, 0]
+    mask = _sdpa_mask(tokens, order, queries)
+    q = c.q.double().transpose(0, 1)
+    s = (q @ keys.permute(1, 2, 0)) / math.sqrt(d)
+    w = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
+    assert np.abs(w2 - (w * w).sum(-1).T.numpy()).max() <= 1e-14
+    q0 = torch.zeros_like(c.q)
+    _, _, w2z = oracle_lib.attn_rows(c.table, q0, c.k_pool, c.v_pool, want_sumw2=True)
+    nvis = mask.sum(-1).numpy().astype(np.float64)
+    assert np.abs(w2z - (1.0 / nvis)[:, None]).max() <= 1e-15
+    t1 = make_table([1], [0], [0], 64, 1, 16, shuffle_rng=None, spare=0)
+    c1 = fill_case("one", t1, rng, torch.float32)
+    _, _, w21 = oracle_lib.attn_rows(t1, c1.q, c1.k_pool, c1.v_pool, want_sumw2=True)
+    assert w21[0, 0] == 1.0
+
+
 # ---------------------------------------------------------------- brute force and golden
 def test_brute_force_python_loops(oracle_lib):
     rng = np.random.default_rng(13)
