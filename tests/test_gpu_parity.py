@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from block_causal_chunk_amd.inputs import fill_case, make_case, make_table
-from helpers import LSE_TOL, check_bf16, check_contract_bf16, check_fp8_contract, f64, sample_rows, stats, to_dev
+from helpers import check_bf16, check_lse, check_contract_bf16, check_fp8_contract, f64, sample_rows, stats, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -58,15 +58,15 @@ def test_small_all_elements(B, O, name, split_k):
     c = make_case(name, small=True)
     print(f"[case] small {name} split_k={split_k}", flush=True)
     out, lse, _ = run(B, c, split_k=split_k)
-    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    ref, ref_lse, ref_w2 = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     if c.io_dtype == torch.float32:
         # fp32 is an I/O format: the contract gates hold against the fp32 inputs, the self gates
         # against the oracle on the bf16-rounded inputs the kernel computes with
         check_contract_bf16(f64(out), ref, name)
         bq, bk, bv = (x.to(torch.bfloat16) for x in (c.q, c.k_pool, c.v_pool))
-        ref, ref_lse = O.attn_rows(c.table, bq, bk, bv)
+        ref, ref_lse, ref_w2 = O.attn_rows(c.table, bq, bk, bv, want_sumw2=True)
     check_bf16(f64(out), ref, name)
-    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
 @pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])
@@ -75,9 +75,9 @@ def test_medium_all_elements(B, O, name, xcd):
     c = medium_case(name)
     print(f"[case] medium {name} xcd={xcd}", flush=True)
     out, lse, att = run(B, c, xcd=xcd)
-    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    ref, ref_lse, ref_w2 = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     check_bf16(f64(out), ref, name)
-    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
 @pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
@@ -90,22 +90,35 @@ def test_merge_of_more_than_four_pieces(B, O, io):
     print(f"[case] medium wave_round split_k=7 io={io}", flush=True)
     out, lse, att = run(B, c, split_k=7)
     assert int(att.plan.describe(0)[6]) > 4  # some item has more than four pieces
-    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)
+    ref, ref_lse, ref_w2 = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     check_bf16(f64(out), ref, "wave_round split 7")
-    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_lse, ref_w2)
+
+
+def head_slice(table, q, k_pool, v_pool, heads):
+    """The same call restricted to `heads` (attention is independent per head): a table with
+    len(heads) heads and the matching slices of Q and the pools."""
+    t = table.copy()
+    t.num_heads = len(heads)
+    hs = list(heads)
+    return t, q[:, hs].contiguous(), k_pool[:, :, hs].contiguous(), v_pool[:, :, hs].contiguous()
 
 
 @pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])
-def test_full_size_sampled_rows(B, O, name):
+def test_full_size_all_rows(B, O, name):
+    """Full size, in the configuration bench.py times.  wan13b_task: every row of every head
+    (4,680 x 12); wave_round and long_rollout: every row of the first and the last head."""
     c = make_case(name)
     print(f"[case] full {name}", flush=True)
     out, lse, _ = run(B, c)  # default plan: the configuration bench.py times
-    rows = sample_rows(c.table.lq, n=32)
-    ref, ref_lse = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, rows=rows)
-    got = f64(out)[rows]
-    assert np.isfinite(f64(out)).all()
-    check_bf16(got, ref, name)
-    assert np.abs(f64(lse).T[rows] - ref_lse).max() <= LSE_TOL
+    got, got_lse = f64(out), f64(lse).T
+    assert np.isfinite(got).all() and np.isfinite(got_lse).all()
+    H = c.table.num_heads
+    heads = list(range(H)) if name == "wan13b_task" else [0, H - 1]
+    t, q, k, v = head_slice(c.table, c.q, c.k_pool, c.v_pool, heads)
+    ref, ref_lse, ref_w2 = O.attn_rows(t, q, k, v, want_sumw2=True)
+    check_bf16(got[:, heads], ref, name)
+    check_lse(got_lse[:, heads], ref_lse, ref_w2, name)
 
 
 def test_degenerate_tables(B, O):
@@ -125,9 +138,9 @@ def test_degenerate_tables(B, O):
         c = fill_case("deg", t, rng, torch.bfloat16)
         for split in (1, 0, 4):
             out, lse, _ = run(B, c, split_k=split)
-            ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+            ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, want_sumw2=True)
             check_bf16(f64(out), ref, str(tok))
-            assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+            check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
 def _random_table(rng):
@@ -160,7 +173,7 @@ def test_random_tables(B, O, seed):
     _poison_chunks(c, hidden)
     desc = (f"tokens={t.chunk_tokens.tolist()} order={t.chunk_order.tolist()} queries={t.query_chunks.tolist()} "
             f"page={t.page_size} H={t.num_heads} d={t.head_dim} scale={t.softmax_scale} ties={ties}")
-    ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+    ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     q, k, v = to_dev(c)
     H, d = t.num_heads, t.head_dim
     for split in (0, 1, 5):
@@ -169,13 +182,13 @@ def test_random_tables(B, O, seed):
         out, lse = att.fwd(q, k, v, want_lse=True)
         torch.cuda.synchronize()
         check_bf16(f64(out), ref, desc)
-        assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+        check_lse(f64(lse).T, ref_lse, ref_w2)
     print(f"[case] random seed={seed} fp32 I/O {desc}", flush=True)
     att = B.Attention(t, mode=B.WFATTN_WS_FP32, order_ties=int(ties))
     out, lse = att.fwd(q.float(), k.float(), v.float(), want_lse=True)
     torch.cuda.synchronize()
     check_bf16(f64(out), ref, desc)
-    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_lse, ref_w2)
     print(f"[case] random seed={seed} e4m3 {desc}", flush=True)
     att8 = B.Attention(t, mode=B.WFATTN_WS_FP8, order_ties=int(ties))
     rows = k.shape[0] * k.shape[1]
@@ -184,9 +197,9 @@ def test_random_tables(B, O, seed):
     out8, lse8 = att8.fwd_fp8(q8, qs, k8.view(k.shape), ks, v, want_lse=True)
     torch.cuda.synchronize()
     qdq, kdq = _dequantized_case(O, c)
-    ref_dq, ref_dq_lse = O.attn_rows(t, qdq, kdq, c.v_pool)
+    ref_dq, ref_dq_lse, ref_dq_w2 = O.attn_rows(t, qdq, kdq, c.v_pool, want_sumw2=True)
     check_bf16(f64(out8), ref_dq, desc + " e4m3 (dequantized oracle)")
-    assert np.abs(f64(lse8).T - ref_dq_lse).max() <= LSE_TOL
+    check_lse(f64(lse8).T, ref_dq_lse, ref_dq_w2)
 
 
 # ------------------------------------------------------------------ mask variants
@@ -213,7 +226,7 @@ def test_tied_window(B, O):
         t = make_table(tok, order, [5, 3, 4], page, H, d, shuffle_rng=rng, spare=2)
         c = fill_case("tied", t, rng, torch.bfloat16)
         _poison_chunks(c, [6])
-        ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+        ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, want_sumw2=True)
         q, k, v = to_dev(c)
         for split in (1, 0, 3):
             print(f"[case] tied window {tok} page={page} H={H} d={d} split_k={split}", flush=True)
@@ -222,7 +235,7 @@ def test_tied_window(B, O):
             torch.cuda.synchronize()
             assert np.isfinite(f64(out)).all()
             check_bf16(f64(out), ref, "tied")
-            assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+            check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
 def test_tied_window_e4m3_and_gated(B, O):
@@ -284,9 +297,9 @@ def test_store_rank_query_shape(B, O):
     out, lse, _ = run(B, c)
     assert np.isfinite(f64(out)).all()
     rows = sample_rows(t.lq, n=48)
-    ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool, rows=rows)
+    ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, rows=rows, want_sumw2=True)
     check_bf16(f64(out)[rows], ref, "store")
-    assert np.abs(f64(lse).T[rows] - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T[rows], ref_lse, ref_w2)
 
 
 # ------------------------------------------------------------------ publish + gate
@@ -355,9 +368,9 @@ def test_publish_then_gated_forward_on_two_streams(B, O):
     B.wfattn_fwd_gated(att.plan, q, kp_dev, vp_dev, out, lse, att.ws, flags, need, 1000, status, stream=consumer)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
-    ref, ref_lse = O.attn_rows(t, c.q, c.k_pool, c.v_pool)
+    ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     check_bf16(f64(out), ref, "gated")
-    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
 def test_gate_skips_items_of_unpublished_chunks(B, O):
@@ -492,9 +505,9 @@ def test_pool_beyond_4gib(B, O):
     print("[case] pools of 4.4 GB, pages past 4 GiB", flush=True)
     out, lse = att.fwd(c.q.cuda(), kp, vp, want_lse=True)
     torch.cuda.synchronize()
-    ref, ref_lse = O.attn_rows(compact, c.q, c.k_pool, c.v_pool)
+    ref, ref_lse, ref_w2 = O.attn_rows(compact, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     check_bf16(f64(out), ref, "beyond 4 GiB")
-    assert np.abs(f64(lse).T - ref_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_lse, ref_w2)
     # publish chunk 1 (130 tokens, one page) into its high page and read the page back
     sk, sv = _chunk_rows(c, 1)
     page = int(big.page_ids[int(big.page_offsets[1])])
@@ -747,9 +760,9 @@ def test_fp8_small_all_elements(B, O, name, split_k):
     out, lse = run_fp8(B, c, split_k)
     got = f64(out)
     qdq, kdq = _dequantized_case(O, c)
-    ref_dq, ref_dq_lse = O.attn_rows(c.table, qdq, kdq, c.v_pool)  # diagnostic: the kernel's own arithmetic
+    ref_dq, ref_dq_lse, ref_dq_w2 = O.attn_rows(c.table, qdq, kdq, c.v_pool, want_sumw2=True)  # diagnostic: the kernel's own arithmetic
     check_bf16(got, ref_dq, name + " (dequantized oracle)")
-    assert np.abs(f64(lse).T - ref_dq_lse).max() <= LSE_TOL
+    check_lse(f64(lse).T, ref_dq_lse, ref_dq_w2)
     ref, _ = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool)  # contract: unquantized inputs
     s = stats(got, ref)
     print(f"fp8 vs unquantized oracle: {s}", flush=True)
@@ -965,19 +978,25 @@ def test_full_size_rope_publish_bit_exact(B, O, k_e4m3):
     assert flags.cpu().tolist() == [0, 0, 0, 4]
 
 
-def test_fp8_full_size_sampled_rows(B, O):
+def test_fp8_full_size_all_rows(B, O):
+    """wan14b_fp8 at full size (40 heads): every row of the first and the last head, against the
+    unquantized oracle (contract) and the oracle on the dequantized inputs (self gates)."""
     c = make_case("wan14b_fp8")
     print("[case] fp8 full wan14b_fp8", flush=True)
-    out, _ = run_fp8(B, c)
+    out, lse = run_fp8(B, c)
     got = f64(out)
     assert np.isfinite(got).all()
-    rows = sample_rows(c.table.lq, n=24)
-    ref, _ = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, rows=rows)
-    s = check_fp8_contract(got[rows], ref, "wan14b_fp8")
+    H = c.table.num_heads
+    heads = [0, H - 1]
+    t, q, k, v = head_slice(c.table, c.q, c.k_pool, c.v_pool, heads)
+    ref, _ = O.attn_rows(t, q, k, v)
+    s = check_fp8_contract(got[:, heads], ref, "wan14b_fp8")
     print("fp8 contract stats", s)
     qdq, kdq = _dequantized_case(O, c)
-    ref_dq, _ = O.attn_rows(c.table, qdq, kdq, c.v_pool, rows=rows)
-    check_bf16(got[rows], ref_dq, "wan14b_fp8 (dequantized oracle)")
+    t, qd, kd, vd = head_slice(c.table, torch.from_numpy(qdq), torch.from_numpy(kdq), c.v_pool, heads)
+    ref_dq, ref_dq_lse, ref_dq_w2 = O.attn_rows(t, qd, kd, vd, want_sumw2=True)
+    check_bf16(got[:, heads], ref_dq, "wan14b_fp8 (dequantized oracle)")
+    check_lse(f64(lse).T[:, heads], ref_dq_lse, ref_dq_w2, "wan14b_fp8 (dequantized oracle)")
 
 
 def test_measurement_probes():
