@@ -4,10 +4,15 @@ One step = one wfattn_fwd call (every kernel of the hot path) over one DiT layer
 one chunk-stage task, with inputs resident in HBM; the plan and its upload are built once per
 round and timed separately.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--no-cpu-baseline] [--no-extras]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--no-configs]
+                  [--no-cpu-baseline] [--no-extras]
 
 Default workload: the Wan-1.3B chunk task (H=12, d=128, 4680 query tokens of one chunk against
-18720 keys of the own chunk and three earlier ones, 256-token shuffled pages), bf16.
+18720 keys of the own chunk and three earlier ones, 256-token shuffled pages), bf16.  Before it,
+the same run measures the other full-size workloads (the mixed-noise wave round, the long
+rollout, the 14B-shaped e4m3 task) and the headline workload with a cold Infinity Cache; they go
+into the line's "configs" object.  Every figure is a p50 over the timed calls (the pages report
+p50 over steady ticks); the roofline prices the attention kernel's mean event-timed launch.
 """
 from __future__ import annotations
 
@@ -332,53 +337,34 @@ def cpu_model() -> str:
     return f"{name}, {len(os.sched_getaffinity(0))} logical CPUs available"
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="wan13b_task")
-    ap.add_argument("--split-k", type=int, default=0)
-    ap.add_argument("--xcd-remap", type=int, default=0)
-    ap.add_argument("--cold", action="store_true", help="evict the 256 MB Infinity Cache between steps")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the publish and gated-forward measurements (profiling runs)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds the oracle sample aims at (at least 10)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed steps, run a plain 256 MiB copy kernel (3 times) so that a "
-                         "counter run can scale FETCH_SIZE/WRITE_SIZE against known bytes")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: the library runs on exactly one GPU (it has no collectives and no sharding); "
-              "use --gpus 1", file=sys.stderr)
-        sys.exit(2)
+CONFIG_STEPS, CONFIG_WARMUP = 100, 30  # per workload of the "configs" object
 
-    import numpy as np
+
+def prepare(B, name, split_k=0, xcd_remap=0, dev="cuda:0"):
+    """Build workload `name` on the device, plan it and upload the plan (quantize Q and the K pool
+    for the e4m3 workload): everything a timed call needs, so that the calls of several workloads
+    can then be timed back to back."""
     import torch
 
-    from block_causal_chunk_amd import binding as B
-    from block_causal_chunk_amd.inputs import WORKLOADS, make_case
+    from block_causal_chunk_amd.inputs import make_case
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    B.lib()
-    dev = torch.device("cuda:0")
-    case = make_case(args.workload)
+    case = make_case(name)
     t = case.table
-    fp8 = args.workload == "wan14b_fp8"
+    fp8 = name == "wan14b_fp8"
     f32 = case.io_dtype == torch.float32
     q, k, v = case.q.to(dev), case.k_pool.to(dev), case.v_pool.to(dev)
     H, d = t.num_heads, t.head_dim
 
     tp0 = time.perf_counter()
     mode = B.WFATTN_WS_FP8 if fp8 else (B.WFATTN_WS_FP32 if f32 else B.WFATTN_WS_BF16)
-    att = B.Attention(t, device=dev, mode=mode, split_k=args.split_k, xcd_remap=args.xcd_remap)
+    att = B.Attention(t, device=dev, mode=mode, split_k=split_k, xcd_remap=xcd_remap)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - tp0) * 1e3
     summary = att.plan.describe(0)
 
     out = torch.empty((t.lq, H, d), dtype=torch.bfloat16 if not f32 else torch.float32, device=dev)
     quant_ms = None
+    k8 = ks = None
     if fp8:
         rows = k.shape[0] * k.shape[1]
         kv = k.view(rows, H, d)
@@ -411,20 +397,36 @@ def main():
         def step_marked(ev):
             B.wfattn_fwd_marked(att.plan, dt, q, k, v, out, None, att.ws, ev.cuda_event)
 
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
-    for _ in range(args.warmup):
+    torch.cuda.synchronize()
+    return dict(name=name, case=case, att=att, q=q, k=k, v=v, k8=k8, ks=ks, fp8=fp8, f32=f32, step=step,
+                step_marked=step_marked, plan_ms=plan_ms, summary=summary, quant_ms=quant_ms)
+
+
+def measure(prep, steps, warmup, cold=False, dev="cuda:0"):
+    """Time `steps` calls of a prepared workload after `warmup` untimed ones, each bracketed by HIP
+    events on the launch stream, plus an event the library records between the attention launch
+    and the merge launch.  Returns the figures."""
+    import numpy as np
+    import torch
+    name, case, step, step_marked = prep["name"], prep["case"], prep["step"], prep["step_marked"]
+    t = case.table
+    fp8, f32 = prep["fp8"], prep["f32"]
+    H, d = t.num_heads, t.head_dim
+    plan_ms, summary, quant_ms = prep["plan_ms"], prep["summary"], prep["quant_ms"]
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     # one more event per step, recorded by the library between the attention launch and the merge
     # launch (recorded once here so that it exists), to time the attention kernel on its own
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for ev in mids:
         ev.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         if scratch is not None:
             scratch.fill_(i & 0xFF)  # untimed 512 MB write evicts the Infinity Cache
         starts[i].record()
@@ -432,6 +434,110 @@ def main():
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del scratch
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
+    per_attn = np.array([s.elapsed_time(m) for s, m in zip(starts, mids)])  # the attention kernel alone
+    p50 = float(np.median(per))
+    attn_ms = float(per_attn.mean())
+    flops = effective_flops(t)
+    peak = PEAK_FP8 if fp8 else PEAK_BF16
+    kflops = flops / (attn_ms * 1e-3) / 1e12
+    r = {
+        "workload": name, "cache": "cold" if cold else "warm", "steps": steps, "warmup": warmup,
+        "heads": H, "head_dim": d, "query_tokens": t.lq, "key_tokens": int(sum(int(x) for x in t.chunk_tokens)),
+        "query_chunks": len(t.query_chunks), "page_size": t.page_size,
+        "dtype": "e4m3 QK^T, bf16 PV" if fp8 else ("bf16 (fp32 I/O)" if f32 else "bf16"),
+        "p10_ms": round(float(np.percentile(per, 10)), 4), "p50_ms": round(p50, 4),
+        "p90_ms": round(float(np.percentile(per, 90)), 4), "mean_ms": round(float(per.mean()), 4),
+        "tflops": round(flops / (p50 * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(flops / (p50 * 1e-3) / 1e12 / peak, 4),
+        "tasks_per_s": round(len(t.query_chunks) / (p50 * 1e-3), 1),
+        "effective_gflop_per_step": round(flops / 1e9, 3),
+        "plan_and_upload_ms": round(plan_ms, 3),
+        "plan": {"items": int(summary[0]), "key_tiles": int(summary[1]), "merge_groups": int(summary[2]),
+                 "splits": int(summary[6]), "block_m": int(summary[4]), "block_n": int(summary[5])},
+        # the dominant kernel: effective FLOPs over the attention kernel's own mean event-timed launch
+        "roofline": {"bound": "mfma", "achieved": round(kflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kflops / peak, 4),
+                     "traffic": traffic_from_profiles(name, "attn_fwd_kernel"),
+                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4),
+                     "kernel_p50_ms": round(float(np.median(per_attn)), 4),
+                     "merge_ms": round(float(per.mean()) - attn_ms, 4)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if fp8:
+        # e4m3 Q.K^T at the fp8 rate, P.V at the bf16 rate: the bound the workload's mix allows
+        r["roofline"]["frac_of_mixed_bound"] = round(kflops / PEAK_MIXED, 4)
+        r["roofline"]["mixed_bound"] = PEAK_MIXED
+        r["quantize_k_pool_ms"] = round(quant_ms, 4)
+    staged, unique = gather_bytes(t, 1 if fp8 else 2)
+    traffic = traffic_from_profiles(name)
+    sec = p50 * 1e-3
+    r["gather"] = {"lds_staged_bytes": staged, "lds_staged_gbs": round(staged / sec / 1e9, 1),
+                   "kv_unique_bytes": unique, "kv_unique_gbs": round(unique / sec / 1e9, 1),
+                   "beyond_l2_gbs": None if traffic is None else round(traffic / sec / 1e9, 1),
+                   "beyond_l2_bytes_per_call": traffic}
+    return r
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="wan13b_task")
+    ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--xcd-remap", type=int, default=0)
+    ap.add_argument("--cold", action="store_true", help="evict the 256 MB Infinity Cache between steps")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the headline workload (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the publish and gated-forward measurements (profiling runs)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds the oracle sample aims at (at least 10)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 256 MiB copy kernel (3 times) so that a "
+                         "counter run can scale FETCH_SIZE/WRITE_SIZE against known bytes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: the library runs on exactly one GPU (it has no collectives and no sharding); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_causal_chunk_amd import binding as B
+    from block_causal_chunk_amd.inputs import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    dev = torch.device("cuda:0")
+
+    # Every workload is built and planned first (host work, during which the GPU idles and its
+    # clock falls back); then the calls run back to back: the other full-size workloads and the
+    # headline workload with a cold cache (their figures go into "configs"), and the headline last,
+    # so that its warm-up starts at the clock the chip holds under this load rather than from idle.
+    names = [] if args.no_configs else [n for n in WORKLOADS if n not in (args.workload, "tiny_fp32")]
+    preps = {}
+    for name in names:
+        print(f"bench: building {name}", file=sys.stderr, flush=True)
+        preps[name] = prepare(B, name, dev=dev)
+    print(f"bench: building {args.workload}", file=sys.stderr, flush=True)
+    head = prepare(B, args.workload, split_k=args.split_k, xcd_remap=args.xcd_remap, dev=dev)
+    configs = {}
+    for name in names:
+        print(f"bench: measuring {name}", file=sys.stderr, flush=True)
+        configs[name] = measure(preps[name], CONFIG_STEPS, CONFIG_WARMUP, dev=dev)
+    if names and not args.cold:
+        print(f"bench: measuring {args.workload} (cold cache)", file=sys.stderr, flush=True)
+        configs[args.workload + "_cold"] = measure(head, CONFIG_STEPS // 2, CONFIG_WARMUP, cold=True, dev=dev)
+    print(f"bench: measuring {args.workload} (headline)", file=sys.stderr, flush=True)
+    r = measure(head, args.steps, args.warmup, cold=args.cold, dev=dev)
+    preps.clear()
+    torch.cuda.empty_cache()
+    case, att, t = head["case"], head["att"], head["case"].table
+    q, k, v, k8, ks, fp8, f32 = (head[x] for x in ("q", "k", "v", "k8", "ks", "fp8", "f32"))
+    H, d = t.num_heads, t.head_dim
     if args.copy_calibration:
         # the probe library's plain copy kernel, 256 MiB, so that a counter run can scale its
         # memory counters by what they read for known bytes
@@ -445,32 +551,21 @@ def main():
         if not bool(torch.equal(src, dst)):
             raise RuntimeError("calibration copy is wrong")
         del src, dst
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per call, stream events
-    per_attn = np.array([s.elapsed_time(m) for s, m in zip(starts, mids)])  # the attention kernel alone
     extra = {}
     if not (f32 or args.no_extras):
         extra = publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v)
         extra.update(rope_publish(B, att, t, None if fp8 else k, k8 if fp8 else None, ks if fp8 else None, v))
     exp_peak = exp_peak_per_s()
-    ms = float(per.mean())
-    attn_ms = float(per_attn.mean())
+    p50 = r["p50_ms"]
     flops = effective_flops(t)
-    tflops = flops / (ms * 1e-3) / 1e12  # the whole call (attention + merge): the metric's value
-    kflops = flops / (attn_ms * 1e-3) / 1e12
-    tasks = len(t.query_chunks) / (float(np.median(per)) * 1e-3)  # per the p50 call
-    peak = PEAK_MIXED if fp8 else PEAK_BF16
-    staged, unique = gather_bytes(t, 1 if fp8 else 2)
+    tflops = flops / (p50 * 1e-3) / 1e12  # the whole call (attention + merge) at the p50 call
     exps = flops / (4.0 * d)  # one exponential per unmasked (query row, key, head)
     counters = mfma_counters_from_profiles(args.workload)
+    peak = r["roofline"]["peak"]
     if counters is not None:
         # the roofline peak again at the clock the kernel actually ran at under load
         counters["peak_at_active_clock"] = round(peak * counters["active_clock_ghz"] / 2.4, 1)
-        counters["frac_at_active_clock"] = round(kflops / counters["peak_at_active_clock"], 4)
-    traffic = traffic_from_profiles(args.workload)
-    sec = ms * 1e-3
-    gather = {"lds_staged_bytes": staged, "lds_staged_gbs": round(staged / sec / 1e9, 1),
-              "kv_unique_bytes": unique, "kv_unique_gbs": round(unique / sec / 1e9, 1),
-              "beyond_l2_gbs": None if traffic is None else round(traffic / sec / 1e9, 1)}
+        counters["frac_at_active_clock"] = round(r["roofline"]["achieved"] / counters["peak_at_active_clock"], 4)
     res = {
         "metric": "effective attention TFLOP/s + chunk-tasks/s, Wan-1.3B shape, % MFMA peak",
         "value": round(tflops, 2),
@@ -478,39 +573,36 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": r["p50_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 QK^T, bf16 PV" if fp8 else ("bf16 (fp32 I/O)" if f32 else "bf16"),
+        "dtype": r["dtype"],
         "data": "synthetic, seeded N(0,1) Q/K/V, shuffled 256-token pages",
         "config": {"workload": args.workload, "heads": H, "head_dim": d,
-                   "query_tokens": t.lq, "key_tokens": int(sum(int(x) for x in t.chunk_tokens)),
+                   "query_tokens": t.lq, "key_tokens": r["key_tokens"],
                    "query_chunks": len(t.query_chunks), "page_size": t.page_size,
-                   "cache": "cold" if args.cold else "warm"},
-        "tasks_per_s": round(tasks, 1),
-        "p10_ms": round(float(np.percentile(per, 10)), 4),
-        "p50_ms": round(float(np.percentile(per, 50)), 4),
-        "p90_ms": round(float(np.percentile(per, 90)), 4),
-        "effective_gflop_per_step": round(flops / 1e9, 3),
-        "plan_and_upload_ms": round(plan_ms, 3),
-        "plan": {"items": int(summary[0]), "key_tiles": int(summary[1]), "merge_groups": int(summary[2]),
-                 "splits": int(summary[6]), "block_m": int(summary[4]), "block_n": int(summary[5])},
-        # the dominant kernel: effective FLOPs over the attention kernel's own event-timed duration
-        "roofline": {"bound": "mfma", "achieved": round(kflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(kflops / peak, 4), "traffic": traffic_from_profiles(args.workload, "attn_fwd_kernel"),
-                     "kernel": "attn_fwd_kernel",
-                     "kernel_ms": round(attn_ms, 4), "merge_ms": round(ms - attn_ms, 4)},
+                   "cache": r["cache"]},
+        "value_stat": "p50 of the timed calls",
+        "frac_of_peak": r["frac_of_peak"],
+        "tasks_per_s": r["tasks_per_s"],
+        "p10_ms": r["p10_ms"], "p50_ms": r["p50_ms"], "p90_ms": r["p90_ms"], "mean_ms": r["mean_ms"],
+        "effective_gflop_per_step": r["effective_gflop_per_step"],
+        "plan_and_upload_ms": r["plan_and_upload_ms"],
+        "plan": r["plan"],
+        "roofline": r["roofline"],
         "mfma_counters": counters,
-        "exps_per_s": round(exps / (ms * 1e-3), 1),
+        "exps_per_s": round(exps / (p50 * 1e-3), 1),
         "exp_peak_per_s": round(exp_peak, 1),
-        "exp_frac": round(exps / (ms * 1e-3) / exp_peak, 4),
-        "gather": gather,
-        "wall_s_timed": round(wall, 3),
+        "exp_frac": round(exps / (p50 * 1e-3) / exp_peak, 4),
+        "gather": r["gather"],
+        "wall_s_timed": r["wall_s_timed"],
     }
     if fp8:
-        res["quantize_k_pool_ms"] = round(quant_ms, 4)
+        res["quantize_k_pool_ms"] = r["quantize_k_pool_ms"]
     res.update(extra)
+    if configs:
+        res["configs"] = configs
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
         res["cpu_baseline"]["value"] = round(res["cpu_baseline"]["value"], 6)
