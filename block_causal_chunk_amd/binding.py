@@ -22,8 +22,9 @@ EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_work
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
             "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish", "wfattn_fwd_marked",
-            "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated"]
+            "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated", "wfattn_fwd_noalloc"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
+WFATTN_NOALLOC_MAX_BYTES = 64 << 20
 
 
 class WfattnError(RuntimeError):
@@ -91,6 +92,8 @@ def lib():
         L.wfattn_rope_publish.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz,
                                           vp]
         L.wfattn_rope_publish.restype = i32
+        L.wfattn_fwd_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
+        L.wfattn_fwd_noalloc.restype = i32
         L.wfattn_status_str.argtypes = [i32]
         L.wfattn_status_str.restype = ctypes.c_char_p
         L.wfattn_abi_version.argtypes = []
@@ -239,6 +242,11 @@ def wfattn_fwd_fp8_marked(plan: Plan, q8, q_scale, k8_pool, k_scale, v_pool, out
     _check(lib().wfattn_fwd_fp8_marked(plan.handle, _ptr(q8), _ptr(q_scale), _ptr(k8_pool), _ptr(k_scale),
                                        _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                        attn_done_event, _stream(stream)), "wfattn_fwd_fp8_marked")
+
+
+def wfattn_fwd_noalloc(plan: Plan, dtype: int, q, k_pool, v_pool, out, lse, stream=None):
+    _check(lib().wfattn_fwd_noalloc(plan.handle, int(dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                                    _ptr(lse), _stream(stream)), "wfattn_fwd_noalloc")
 
 
 def wfattn_quantize_fp8(x, rows: int, heads: int, head_dim: int, x8, scales, stream=None):

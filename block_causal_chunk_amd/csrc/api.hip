@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" entry points that touch the device: upload, forward, quantize.
 // Every argument check runs before the first HIP call (see include/wfattn.h for the contract).
 #include <cmath>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -299,3 +300,53 @@ extern "C" wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, i
   return WFATTN_OK;
 }
 
+// ---- forward without allocation ---------------------------------------------------------------
+// The workspace of wfattn_fwd_noalloc is this file-scope device array: every GPU the library runs
+// on holds one copy of it until the process ends.  Host code never passes `scratch` itself to a
+// kernel or a copy (on the host that name is only a stand-in for the symbol); it uses the address
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+namespace {
+
+__device__ __align__(256) uint8_t scratch[WFATTN_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch` (looked up on the first call per device).
+wfattn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WFATTN_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return WFATTN_ERR_DEVICE;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return WFATTN_OK;
+}
+
+}  // namespace
+
+extern "C" wfattn_status wfattn_fwd_noalloc(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
+                                            const void* k_pool, const void* v_pool, void* out, float* lse,
+                                            void* stream) {
+  if (!plan || !q || !k_pool || !v_pool || !out) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  if (dtype != WFATTN_BF16 && dtype != WFATTN_FP32) return WFATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return WFATTN_ERR_UNSUPPORTED;
+  const Plan* P = as_plan(plan);
+  const size_t need = dtype == WFATTN_FP32 ? P->ws_fp32_bytes : P->ws_base_bytes;
+  if (need > static_cast<size_t>(WFATTN_NOALLOC_MAX_BYTES)) return WFATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const wfattn_status st = scratch_of_current_device(&ws);
+  if (st != WFATTN_OK) return st;
+  // this call's work list and page table replace whatever the previous call left in the array;
+  // nothing else in it needs a starting value (split-K partials are written before they are read)
+  if (hipMemcpyAsync(static_cast<char*>(ws) + P->ws_blob, P->blob.data(), P->blob.size() * sizeof(int32_t),
+                     hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WFATTN_ERR_DEVICE;
+  return fwd_impl(plan, dtype, q, k_pool, v_pool, out, lse, ws, WFATTN_NOALLOC_MAX_BYTES, stream, nullptr);
+}

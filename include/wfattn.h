@@ -292,6 +292,25 @@ wfattn_status wfattn_fwd_gated(const wfattn_plan_t* plan, const void* q, const v
                                const uint32_t* flags, const uint32_t* need, int32_t spin_limit,
                                uint32_t* gate_status, void* stream);
 
+/* ---- forward without allocation --------------------------------------------------------------
+ * For callers that cannot allocate device memory or own a workspace: serving loops and harnesses
+ * that forbid hipMalloc, and code that must not allocate while it records work.  wfattn_fwd with
+ * the workspace taken from a device array inside the library (WFATTN_NOALLOC_MAX_BYTES = 64 MiB
+ * per GPU, held until the process ends).  Each call copies the plan's work list and page table
+ * into that array on `stream` (hipMemcpyAsync from the plan's host memory: the plan must stay
+ * alive until the copy has run) and then runs the same kernels as wfattn_fwd, so the results are
+ * those of wfattn_fwd, bit for bit.  It calls no hipMalloc, hipFree or other allocating routine.
+ * All calls on one GPU share its array, which keeps the last call's contents: calls that overlap
+ * on one GPU (two streams, two threads) race and give undefined results; calls ordered on one
+ * stream are safe.  q, k_pool, v_pool, out, lse as wfattn_fwd.
+ * Errors: NULL, INVALID, UNSUPPORTED (dtype, alignment), WORKSPACE (the plan needs more than
+ * WFATTN_NOALLOC_MAX_BYTES: wfattn_workspace_bytes(plan, mode) tells), DEVICE.  Every check but
+ * DEVICE runs before the first HIP call. */
+#define WFATTN_NOALLOC_MAX_BYTES (64u << 20)
+wfattn_status wfattn_fwd_noalloc(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
+                                 const void* k_pool, const void* v_pool, void* out, float* lse,
+                                 void* stream);
+
 /* Static string naming a status. */
 const char* wfattn_status_str(wfattn_status status);
 

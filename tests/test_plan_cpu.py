@@ -398,3 +398,23 @@ def test_schedule_full_size_tables_and_xcd_grouping(B):
     t = make_table([4680] * 4, [0, 1, 2, 3], [3], 256, 12, 128)
     tiles = B.wfattn_plan(t, split_k=1).describe(2).reshape(-1, 2)
     assert tiles.shape[0] == 4 * (18 * 4 + 2) and tiles[:, 1].sum() == 4 * 4680
+
+
+def test_noalloc_forward_checks_before_any_device_call(B):
+    """wfattn_fwd_noalloc decides NULL, INVALID, UNSUPPORTED and WORKSPACE (a plan needing more than
+    its 64 MiB device array) on the host, before its first HIP call."""
+    from block_causal_chunk_amd.inputs import WORKLOADS
+    L = B.lib()
+    w = WORKLOADS["wan13b_task"]
+    t = make_table(w["tokens"], list(range(len(w["tokens"]))), w["queries"], w["page"], w["H"], w["d"],
+                   spare=w["spare"])
+    plan = B.wfattn_plan(t)
+    fake = 1 << 20  # aligned, never dereferenced
+    assert plan.workspace_bytes(B.WFATTN_WS_BF16) <= B.WFATTN_NOALLOC_MAX_BYTES
+    assert plan.workspace_bytes(B.WFATTN_WS_FP32) > B.WFATTN_NOALLOC_MAX_BYTES
+    assert L.wfattn_fwd_noalloc(plan.handle, B.WFATTN_FP32, fake, fake, fake, fake, None, None) == B.WFATTN_ERR_WORKSPACE
+    assert L.wfattn_fwd_noalloc(None, B.WFATTN_BF16, fake, fake, fake, fake, None, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd_noalloc(plan.handle, B.WFATTN_BF16, fake, None, fake, fake, None, None) == B.WFATTN_ERR_NULL
+    assert L.wfattn_fwd_noalloc(plan.handle, 7, fake, fake, fake, fake, None, None) == B.WFATTN_ERR_UNSUPPORTED
+    assert L.wfattn_fwd_noalloc(plan.handle, B.WFATTN_BF16, fake + 8, fake, fake, fake, None, None) == \
+        B.WFATTN_ERR_UNSUPPORTED
