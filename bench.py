@@ -41,10 +41,10 @@ def effective_flops(table) -> float:
     return 4.0 * t.head_dim * t.num_heads * tot
 
 
-def gather_bytes(table, k_bytes: int) -> tuple:
+def gather_bytes(table, k_bytes: int, v_bytes: int = 2) -> tuple:
     """(K/V bytes staged into LDS per call, unique visible K/V bytes per call).  Every query tile of
     up to 256 rows of one head loads the 64-key tiles of its visible prefix (a tile never crosses a
-    page), K at k_bytes and V at 2 bytes per element."""
+    page), K at k_bytes and V at v_bytes per element."""
     t = table
     d, H = t.head_dim, t.num_heads
     tiles = []
@@ -59,8 +59,8 @@ def gather_bytes(table, k_bytes: int) -> tuple:
     for a in t.query_chunks:
         pre = [b for b in range(t.num_chunks) if t.chunk_order[b] <= t.chunk_order[a]]
         visible.update(pre)
-        staged += H * -(-int(t.chunk_tokens[a]) // 256) * sum(tiles[b] for b in pre) * 64 * d * (k_bytes + 2)
-    unique = sum(int(t.chunk_tokens[b]) for b in visible) * H * d * (k_bytes + 2)
+        staged += H * -(-int(t.chunk_tokens[a]) // 256) * sum(tiles[b] for b in pre) * 64 * d * (k_bytes + v_bytes)
+    unique = sum(int(t.chunk_tokens[b]) for b in visible) * H * d * (k_bytes + v_bytes)
     return staged, unique
 
 
@@ -350,7 +350,8 @@ def prepare(B, name, split_k=0, xcd_remap=0, dev="cuda:0"):
 
     case = make_case(name)
     t = case.table
-    fp8 = name == "wan14b_fp8"
+    fp8 = name in ("wan14b_fp8", "wan14b_fp8kv")
+    kv8 = name == "wan14b_fp8kv"  # V stored as e4m3 too
     f32 = case.io_dtype == torch.float32
     q, k, v = case.q.to(dev), case.k_pool.to(dev), case.v_pool.to(dev)
     H, d = t.num_heads, t.head_dim
@@ -382,12 +383,20 @@ def prepare(B, name, split_k=0, xcd_remap=0, dev="cuda:0"):
         torch.cuda.synchronize()
         quant_ms = e0.elapsed_time(e1) / 10
         k8 = k8.view(k.shape)
+        if kv8:
+            v8, vs = B.quantize_v_fp8(v)
 
-        def step():
-            B.wfattn_fwd_fp8(att.plan, q8, qs, k8, ks, v, out, None, att.ws)
+            def step():
+                B.wfattn_fwd_fp8kv(att.plan, q8, qs, k8, ks, v8, vs, out, None, att.ws)
 
-        def step_marked(ev):
-            B.wfattn_fwd_fp8_marked(att.plan, q8, qs, k8, ks, v, out, None, att.ws, ev.cuda_event)
+            def step_marked(ev):
+                B.wfattn_fwd_fp8kv_marked(att.plan, q8, qs, k8, ks, v8, vs, out, None, att.ws, ev.cuda_event)
+        else:
+            def step():
+                B.wfattn_fwd_fp8(att.plan, q8, qs, k8, ks, v, out, None, att.ws)
+
+            def step_marked(ev):
+                B.wfattn_fwd_fp8_marked(att.plan, q8, qs, k8, ks, v, out, None, att.ws, ev.cuda_event)
     else:
         dt = B.WFATTN_FP32 if f32 else B.WFATTN_BF16
 
@@ -398,7 +407,7 @@ def prepare(B, name, split_k=0, xcd_remap=0, dev="cuda:0"):
             B.wfattn_fwd_marked(att.plan, dt, q, k, v, out, None, att.ws, ev.cuda_event)
 
     torch.cuda.synchronize()
-    return dict(name=name, case=case, att=att, q=q, k=k, v=v, k8=k8, ks=ks, fp8=fp8, f32=f32, step=step,
+    return dict(name=name, case=case, att=att, q=q, k=k, v=v, k8=k8, ks=ks, fp8=fp8, kv8=kv8, f32=f32, step=step,
                 step_marked=step_marked, plan_ms=plan_ms, summary=summary, quant_ms=quant_ms)
 
 
@@ -446,7 +455,8 @@ def measure(prep, steps, warmup, cold=False, dev="cuda:0"):
         "workload": name, "cache": "cold" if cold else "warm", "steps": steps, "warmup": warmup,
         "heads": H, "head_dim": d, "query_tokens": t.lq, "key_tokens": int(sum(int(x) for x in t.chunk_tokens)),
         "query_chunks": len(t.query_chunks), "page_size": t.page_size,
-        "dtype": "e4m3 QK^T, bf16 PV" if fp8 else ("bf16 (fp32 I/O)" if f32 else "bf16"),
+        "dtype": ("e4m3 Q/K/V storage, e4m3 QK^T, bf16 PV" if prep["kv8"] else "e4m3 QK^T, bf16 PV") if fp8
+        else ("bf16 (fp32 I/O)" if f32 else "bf16"),
         "p10_ms": round(float(np.percentile(per, 10)), 4), "p50_ms": round(p50, 4),
         "p90_ms": round(float(np.percentile(per, 90)), 4), "mean_ms": round(float(per.mean()), 4),
         "tflops": round(flops / (p50 * 1e-3) / 1e12, 2),
@@ -470,7 +480,7 @@ def measure(prep, steps, warmup, cold=False, dev="cuda:0"):
         r["roofline"]["frac_of_mixed_bound"] = round(kflops / PEAK_MIXED, 4)
         r["roofline"]["mixed_bound"] = PEAK_MIXED
         r["quantize_k_pool_ms"] = round(quant_ms, 4)
-    staged, unique = gather_bytes(t, 1 if fp8 else 2)
+    staged, unique = gather_bytes(t, 1 if fp8 else 2, 1 if prep["kv8"] else 2)
     traffic = traffic_from_profiles(name)
     sec = p50 * 1e-3
     r["gather"] = {"lds_staged_bytes": staged, "lds_staged_gbs": round(staged / sec / 1e9, 1),

@@ -22,7 +22,8 @@ EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_work
             "wfattn_plan_upload", "wfattn_plan_describe", "wfattn_fwd", "wfattn_fwd_fp8",
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
             "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish", "wfattn_fwd_marked",
-            "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated", "wfattn_fwd_noalloc"]
+            "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated", "wfattn_fwd_noalloc", "wfattn_quantize_v_fp8",
+            "wfattn_fwd_fp8kv", "wfattn_fwd_fp8kv_marked"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 WFATTN_NOALLOC_MAX_BYTES = 64 << 20
 
@@ -92,6 +93,12 @@ def lib():
         L.wfattn_rope_publish.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz,
                                           vp]
         L.wfattn_rope_publish.restype = i32
+        L.wfattn_quantize_v_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.wfattn_quantize_v_fp8.restype = i32
+        L.wfattn_fwd_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.wfattn_fwd_fp8kv.restype = i32
+        L.wfattn_fwd_fp8kv_marked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.wfattn_fwd_fp8kv_marked.restype = i32
         L.wfattn_fwd_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
         L.wfattn_fwd_noalloc.restype = i32
         L.wfattn_status_str.argtypes = [i32]
@@ -249,6 +256,25 @@ def wfattn_fwd_noalloc(plan: Plan, dtype: int, q, k_pool, v_pool, out, lse, stre
                                     _ptr(lse), _stream(stream)), "wfattn_fwd_noalloc")
 
 
+def wfattn_quantize_v_fp8(v, rows: int, heads: int, head_dim: int, v8, scales, stream=None):
+    _check(lib().wfattn_quantize_v_fp8(_ptr(v), int(rows), int(heads), int(head_dim), _ptr(v8), _ptr(scales),
+                                       _stream(stream)), "wfattn_quantize_v_fp8")
+
+
+def wfattn_fwd_fp8kv(plan: Plan, q8, q_scale, k8_pool, k_scale, v8_pool, v_scale, out, lse, ws, stream=None):
+    _check(lib().wfattn_fwd_fp8kv(plan.handle, _ptr(q8), _ptr(q_scale), _ptr(k8_pool), _ptr(k_scale), _ptr(v8_pool),
+                                  _ptr(v_scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "wfattn_fwd_fp8kv")
+
+
+def wfattn_fwd_fp8kv_marked(plan: Plan, q8, q_scale, k8_pool, k_scale, v8_pool, v_scale, out, lse, ws,
+                            attn_done_event: int, stream=None):
+    _check(lib().wfattn_fwd_fp8kv_marked(plan.handle, _ptr(q8), _ptr(q_scale), _ptr(k8_pool), _ptr(k_scale),
+                                         _ptr(v8_pool), _ptr(v_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                         ws.numel() * ws.element_size(), attn_done_event, _stream(stream)),
+           "wfattn_fwd_fp8kv_marked")
+
+
 def wfattn_quantize_fp8(x, rows: int, heads: int, head_dim: int, x8, scales, stream=None):
     _check(lib().wfattn_quantize_fp8(_ptr(x), int(rows), int(heads), int(head_dim), _ptr(x8), _ptr(scales),
                                      _stream(stream)), "wfattn_quantize_fp8")
@@ -282,6 +308,17 @@ class Attention:
         wfattn_fwd(self.plan, dt, q, k_pool, v_pool, out, lse, self.ws, stream)
         return out, lse
 
+    def fwd_fp8kv(self, q8, q_scale, k8_pool, k_scale, v8_pool, v_scale, out=None, lse=None, want_lse=False,
+                  stream=None):
+        import torch
+        H, d = int(self.table.num_heads), int(self.table.head_dim)
+        if out is None:
+            out = torch.empty((self.lq, H, d), dtype=torch.bfloat16, device=v8_pool.device)
+        if lse is None and want_lse:
+            lse = torch.empty((H, self.lq), dtype=torch.float32, device=v8_pool.device)
+        wfattn_fwd_fp8kv(self.plan, q8, q_scale, k8_pool, k_scale, v8_pool, v_scale, out, lse, self.ws, stream)
+        return out, lse
+
     def fwd_fp8(self, q8, q_scale, k8_pool, k_scale, v_pool, out=None, lse=None, want_lse=False, stream=None):
         import torch
         H, d = int(self.table.num_heads), int(self.table.head_dim)
@@ -291,6 +328,18 @@ class Attention:
             lse = torch.empty((H, self.lq), dtype=torch.float32, device=v_pool.device)
         wfattn_fwd_fp8(self.plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, self.ws, stream)
         return out, lse
+
+
+def quantize_v_fp8(v_pool, stream=None):
+    """bf16 V pool [pages, page_size, H, d] -> (e4m3 V pool uint8 [pages*page_size/64, H, d, 64],
+    scales f32 [pages*page_size/64, H]) in the layout of the e4m3 K/V forward."""
+    import torch
+    rows = v_pool.shape[0] * v_pool.shape[1]
+    H, d = v_pool.shape[2], v_pool.shape[3]
+    v8 = torch.empty((rows // 64, H, d, 64), dtype=torch.uint8, device=v_pool.device)
+    sc = torch.empty((rows // 64, H), dtype=torch.float32, device=v_pool.device)
+    wfattn_quantize_v_fp8(v_pool, rows, H, d, v8, sc, stream)
+    return v8, sc
 
 
 def quantize_fp8(x, stream=None):

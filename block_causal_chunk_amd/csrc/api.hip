@@ -98,14 +98,16 @@ wfattn_status fwd_impl(const wfattn_plan_t* plan, wfattn_dtype dtype, const void
   return WFATTN_OK;
 }
 
+// v_scale == nullptr: v_pool is the bf16 pool; else v_pool is the e4m3 V pool ([pool_rows / 64,
+// H, d, 64] codes) with those scales
 wfattn_status fwd8_impl(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale, const uint8_t* k8_pool,
-                        const float* k_scale, const void* v_pool, void* out, float* lse, void* ws, size_t ws_bytes,
-                        void* stream, const Gate* gate, hipEvent_t mark) {
+                        const float* k_scale, const void* v_pool, const float* v_scale, void* out, float* lse,
+                        void* ws, size_t ws_bytes, void* stream, const Gate* gate, hipEvent_t mark) {
   if (!plan || !q8 || !q_scale || !k8_pool || !k_scale || !v_pool || !out) return WFATTN_ERR_NULL;
   if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
   if (!ws) return WFATTN_ERR_WORKSPACE;
   if (!aligned(q8, 16) || !aligned(k8_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) || !aligned(q_scale, 4) ||
-      !aligned(k_scale, 4) || !aligned(lse, 4) || !aligned(ws, 256))
+      !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(lse, 4) || !aligned(ws, 256))
     return WFATTN_ERR_UNSUPPORTED;
   const Plan* P = as_plan(plan);
   if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
@@ -115,7 +117,12 @@ wfattn_status fwd8_impl(const wfattn_plan_t* plan, const uint8_t* q8, const floa
   fp.q_scale = q_scale;
   fp.k8 = k8_pool;
   fp.k_scale = k_scale;
-  fp.v = static_cast<const uint16_t*>(v_pool);
+  if (v_scale) {
+    fp.v8 = static_cast<const uint8_t*>(v_pool);
+    fp.v_scale = v_scale;
+  } else {
+    fp.v = static_cast<const uint16_t*>(v_pool);
+  }
   fp.out = out;
   fp.lse = lse;
   if (gate) {
@@ -124,7 +131,8 @@ wfattn_status fwd8_impl(const wfattn_plan_t* plan, const uint8_t* q8, const floa
     fp.gate_status = gate->status;
     fp.gate_spin = gate->spin;
   }
-  if (launch_attn_fp8(fp, P->head_dim, P->n_wgs, s) != hipSuccess) return WFATTN_ERR_DEVICE;
+  const hipError_t e = v_scale ? launch_attn_fp8kv(fp, P->head_dim, P->n_wgs, s) : launch_attn_fp8(fp, P->head_dim, P->n_wgs, s);
+  if (e != hipSuccess) return WFATTN_ERR_DEVICE;
   if (mark && hipEventRecord(mark, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   if (launch_combine(fp, P->head_dim, false, P->n_groups, s) != hipSuccess) return WFATTN_ERR_DEVICE;
   return WFATTN_OK;
@@ -180,7 +188,26 @@ extern "C" wfattn_status wfattn_publish_kv(const wfattn_plan_t* plan, int32_t ch
 extern "C" wfattn_status wfattn_fwd_fp8(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
                                         const uint8_t* k8_pool, const float* k_scale, const void* v_pool, void* out,
                                         float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, nullptr, nullptr);
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, nullptr, out, lse, ws, ws_bytes, stream, nullptr,
+                   nullptr);
+}
+
+extern "C" wfattn_status wfattn_fwd_fp8kv(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                                          const uint8_t* k8_pool, const float* k_scale, const uint8_t* v8_pool,
+                                          const float* v_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  if (!v_scale) return WFATTN_ERR_NULL;
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v8_pool, v_scale, out, lse, ws, ws_bytes, stream, nullptr,
+                   nullptr);
+}
+
+extern "C" wfattn_status wfattn_fwd_fp8kv_marked(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                                                 const uint8_t* k8_pool, const float* k_scale, const uint8_t* v8_pool,
+                                                 const float* v_scale, void* out, float* lse, void* ws,
+                                                 size_t ws_bytes, void* attn_done_event, void* stream) {
+  if (!v_scale || !attn_done_event) return WFATTN_ERR_NULL;
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v8_pool, v_scale, out, lse, ws, ws_bytes, stream, nullptr,
+                   static_cast<hipEvent_t>(attn_done_event));
 }
 
 extern "C" wfattn_status wfattn_fwd_fp8_gated(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
@@ -193,7 +220,7 @@ extern "C" wfattn_status wfattn_fwd_fp8_gated(const wfattn_plan_t* plan, const u
   if (!aligned(flags, 4) || !aligned(need, 4) || !aligned(gate_status, 4)) return WFATTN_ERR_UNSUPPORTED;
   if (!aligned(k8_pool, 256) || !aligned(v_pool, 256)) return WFATTN_ERR_UNSUPPORTED;  // no line spans two pages
   const Gate g{flags, need, gate_status, spin_limit};
-  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, &g, nullptr);
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, nullptr, out, lse, ws, ws_bytes, stream, &g, nullptr);
 }
 
 extern "C" wfattn_status wfattn_fwd_marked(const wfattn_plan_t* plan, wfattn_dtype dtype, const void* q,
@@ -209,7 +236,7 @@ extern "C" wfattn_status wfattn_fwd_fp8_marked(const wfattn_plan_t* plan, const 
                                                void* out, float* lse, void* ws, size_t ws_bytes,
                                                void* attn_done_event, void* stream) {
   if (!attn_done_event) return WFATTN_ERR_NULL;
-  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, out, lse, ws, ws_bytes, stream, nullptr,
+  return fwd8_impl(plan, q8, q_scale, k8_pool, k_scale, v_pool, nullptr, out, lse, ws, ws_bytes, stream, nullptr,
                    static_cast<hipEvent_t>(attn_done_event));
 }
 
@@ -284,6 +311,20 @@ extern "C" wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t 
   return launch_rope_publish(rp, tokens, P->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
              ? WFATTN_OK
              : WFATTN_ERR_DEVICE;
+}
+
+extern "C" wfattn_status wfattn_quantize_v_fp8(const void* v_bf16, int64_t rows, int32_t heads, int32_t head_dim,
+                                               uint8_t* v8, float* scales, void* stream) {
+  if (!v_bf16 || !v8 || !scales) return WFATTN_ERR_NULL;
+  if (head_dim != 64 && head_dim != 128) return WFATTN_ERR_UNSUPPORTED;
+  if (rows < 0 || rows % 64 != 0 || heads < 1) return WFATTN_ERR_RANGE;
+  if (rows / 64 * static_cast<int64_t>(heads) > INT32_MAX) return WFATTN_ERR_RANGE;
+  if (!aligned(v_bf16, 16) || !aligned(v8, 16) || !aligned(scales, 4)) return WFATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return WFATTN_OK;
+  if (launch_quantize_v_fp8(static_cast<const uint16_t*>(v_bf16), rows, heads, head_dim, v8, scales,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WFATTN_ERR_DEVICE;
+  return WFATTN_OK;
 }
 
 extern "C" wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads, int32_t head_dim,

@@ -66,13 +66,18 @@ __device__ __forceinline__ void static_for(F&& f) {
 // address and one precomputed VGPR offset per load.  Rows past the tile's valid keys re-read the
 // last valid row: finite data whose scores are masked to -inf and whose V rows then carry weight
 // 0, so the pool's padding slots are never read.
-template <int D, bool FP8>
+//
+// V8 (e4m3 V): a key tile's V is one contiguous block of the e4m3 V pool, [D channels][64 keys]
+// of one head (the layout wfattn_quantize_v_fp8 writes, codes of keys past a chunk's end 0), so
+// its fill is a plain copy of D*64 bytes with no ragged variant; rows of the LDS copy are channels.
+template <int D, bool FP8, bool V8 = false>
 struct TileLoader {
   static constexpr int KB = FP8 ? D : 2 * D;    // bytes per K row
   static constexpr int KG = KB / 16;            // 16-byte granules per K row
   static constexpr int VG = D / 8;              // 16-byte granules per V row
+  static constexpr int VBYTES = V8 ? BN * D : BN * D * 2;  // bytes of one V tile
   static constexpr int KI = BN * KB / 1024 / 4; // 1 KB loads per wave for K
-  static constexpr int VI = BN * D * 2 / 1024 / 4;
+  static constexpr int VI = VBYTES / 1024 / 4;
 
   uint32_t koff[KI], voff[VI];
   int wave_u;  // wave index, uniform
@@ -94,9 +99,23 @@ struct TileLoader {
   }
   __device__ __forceinline__ static uint32_t v_src(int wave, int j, int lane, int nvalid, int head, int H) {
     const int chunk = (wave * VI + j) * 64 + lane;
-    const int row = chunk / VG, g = swz<D>(row, chunk % VG);
-    const int src = row < nvalid ? row : nvalid - 1;
-    return (uint32_t)((src * H + head) * 2 * D + g * 16);
+    if constexpr (V8) {  // row = channel, 4 granules of 16 keys; nvalid, head, H: see v_base
+      const int c = chunk / 4;
+      return (uint32_t)(c * 64 + v8swz(c, chunk % 4) * 16);
+    } else {
+      const int row = chunk / VG, g = swz<D>(row, chunk % VG);
+      const int src = row < nvalid ? row : nvalid - 1;
+      return (uint32_t)((src * H + head) * 2 * D + g * 16);
+    }
+  }
+  // e4m3 V tile in LDS: row c (a channel) holds 64 key bytes as 4 granules; physical granule p
+  // holds logical granule p ^ ((c / 2) mod 4), so the 8 lanes of one 128-byte read phase
+  // (channels c .. c+7, one logical granule) touch 8 distinct 16-byte bank groups.
+  __device__ __forceinline__ static int v8swz(int c, int g) { return g ^ ((c >> 1) & 3); }
+  // first byte of the V tile whose first key is pool row row0
+  __device__ __forceinline__ static const uint8_t* v_base(const uint8_t* vpool, int row0, int head, int H) {
+    if constexpr (V8) return vpool + ((size_t)(row0 / 64) * H + head) * (size_t)(64 * D);
+    else return vpool + (size_t)row0 * H * 2 * D;
   }
 
   __device__ __forceinline__ void init(int head, int H) {
@@ -137,9 +156,9 @@ struct TileLoader {
     }
   }
   __device__ __forceinline__ void fill_v(const uint8_t* vpool, int row0, int nvalid, int head, int H, uint32_t lds) const {
-    const uint8_t* base = vpool + (size_t)row0 * H * 2 * D;
+    const uint8_t* base = v_base(vpool, row0, head, H);
     const int wave = wave_u;
-    if (nvalid == BN) {
+    if (V8 || nvalid == BN) {
 #pragma unroll
       for (int j = 0; j < VI; ++j) dma16(lds + (wave * VI + j) * 1024, voff[j], base);
     } else {
@@ -216,12 +235,19 @@ __host__ __device__ constexpr int v_first_use(int t, int ns, int np) {
 // every P of the row; if some l reaches 2^64 (some score exceeded the first tile's max by more
 // than 44 natural-log units) the segment is recomputed against the true row max, found by a
 // score-only sweep, which no score exceeds.
-template <int D, bool FP8, bool OUT_F32, bool GATED>
+//
+// V8 (e4m3 K/V storage, with FP8): V tiles are e4m3 codes with one fp32 scale s_v per (64-key
+// tile, head).  Each code converts exactly to bf16 and P.V stays a bf16 MFMA; the scale is folded
+// into the weights instead, P' = exp2(s*c - (m - log2 s_v)) = s_v * P (one reference shift per
+// tile and row), so sum_j P'_j code_j = sum_j P_j v_j, and the row sum adds each tile's sum of the
+// rounded P' times 1/s_v, keeping l the sum of the weights that multiply V.
+template <int D, bool FP8, bool OUT_F32, bool GATED, bool V8 = false>
 __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* items, int item, int kt0, int kt1,
                                             int slot, const int32_t* tiles,
-                                            uint8_t (*smem_k)[BN * TileLoader<D, FP8>::KB], uint16_t (*smem_v)[BN * D],
-                                            int* redo_flags) {
-  using Loader = TileLoader<D, FP8>;
+                                            uint8_t (*smem_k)[BN * TileLoader<D, FP8, V8>::KB],
+                                            uint8_t (*smem_v)[TileLoader<D, FP8, V8>::VBYTES], int* redo_flags) {
+  static_assert(!V8 || (FP8 && !GATED && !OUT_F32), "e4m3 V comes with e4m3 scores, ungated, bf16 out");
+  using Loader = TileLoader<D, FP8, V8>;
   constexpr int KI = Loader::KI, VI = Loader::VI;
   const int head = ld_const(items, item * kItemInts + 0), q_row0 = ld_const(items, item * kItemInts + 1);
   const int q_rows = ld_const(items, item * kItemInts + 2), qsb = ld_const(items, item * kItemInts + 3);
@@ -238,7 +264,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   Loader ld;
   ld.init(head, H);
   const uint8_t* kpool = FP8 ? p.k8 : reinterpret_cast<const uint8_t*>(p.k);
-  const uint8_t* vpool = reinterpret_cast<const uint8_t*>(p.v);
+  const uint8_t* vpool = V8 ? p.v8 : reinterpret_cast<const uint8_t*>(p.v);
   // Q^T as the B operand of S^T = K.Q^T.  bf16: lane holds query row r, channels 16*ks + 8*hi .. +7;
   // e4m3: channels 64*ks + 32*hi .. +31.
   constexpr int QREGS = FP8 ? D / 64 : D / 16;
@@ -288,7 +314,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   };
   // V^T operand of (d block cb, 16-key step k2 of the tile) through two transposed LDS reads
   const int tq = lane & 15, G = lane >> 4;
-  auto v_op = [&](const uint16_t* sv, int cb, int k2) -> bf16x8 {
+  auto v_op = [&](const uint8_t* sv8, int cb, int k2) -> bf16x8 {
+    const uint16_t* sv = reinterpret_cast<const uint16_t*>(sv8);
     const int row = 16 * k2 + 8 * hi + (tq >> 2);
     const int col = 32 * cb + 16 * (G & 1) + 4 * (tq & 3);
     const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WF_LDS i16x4*)(sv + lds_off<D>(row, col)));
@@ -296,6 +323,29 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     // whole-vector concatenation: element-wise 16-bit inserts are lowered wrongly by this
     // compiler (they reuse the first dword of each transposed read)
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // e4m3 V^T operands of (d block cb, half h): one 16-byte read of channel 32cb + l32 holds the
+  // keys of both 16-key steps of the half that this lane feeds (the V8 block stores each half's
+  // 8-key groups in the order 0, 2, 1, 3): bytes 0-7 are keys 32h + 8hi + 0..7, bytes 8-15 keys
+  // 32h + 16 + 8hi + 0..7.
+  auto v8_raw = [&](const uint8_t* sv, int cb, int h) -> i32x4 {
+    const int c = 32 * cb + l32;
+    return *reinterpret_cast<const i32x4*>(sv + c * 64 + Loader::v8swz(c, 2 * h + hi) * 16);
+  };
+  // e4m3 codes -> bf16 (exact: 4 significant bits, exponents within bf16's range)
+  auto v8_cvt = [&](const i32x4& r, bf16x8& a, bf16x8& b) {
+    const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[0], 1.f, false);
+    const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[0], 1.f, true);
+    const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[1], 1.f, false);
+    const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[1], 1.f, true);
+    const bf16x2 w4 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[2], 1.f, false);
+    const bf16x2 w5 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[2], 1.f, true);
+    const bf16x2 w6 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[3], 1.f, false);
+    const bf16x2 w7 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)r[3], 1.f, true);
+    a = __builtin_shufflevector(__builtin_shufflevector(w0, w1, 0, 1, 2, 3), __builtin_shufflevector(w2, w3, 0, 1, 2, 3),
+                                0, 1, 2, 3, 4, 5, 6, 7);
+    b = __builtin_shufflevector(__builtin_shufflevector(w4, w5, 0, 1, 2, 3), __builtin_shufflevector(w6, w7, 0, 1, 2, 3),
+                                0, 1, 2, 3, 4, 5, 6, 7);
   };
   // Score MFMAs are inline asm so that Q^T can stay in AGPRs as their B operand (the builtins
   // would copy it into VGPRs, which the two score halves, P and the operands need).  The compiler
@@ -375,11 +425,12 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     float t[32];
     uint32_t pw[16];
   };
-  auto valu_op = [&](auto kc, ValuState& st, const f32x16 (&s)[2], const float (&cm)[2]) {
+  // mo: the reference the exponent subtracts (m, or for e4m3 V the tile's shifted reference)
+  auto valu_op = [&](auto kc, ValuState& st, const f32x16 (&s)[2], const float (&cm)[2], const float (&mo)[2]) {
     constexpr int k = decltype(kc)::value;
     constexpr int kind = kValu.kind[k], e = kValu.idx[k];
     if constexpr (kind == OP_F) {
-      st.t[e] = fmaf(s[e >> 4][e & 15], cm[e >> 4], -m[e >> 4]);
+      st.t[e] = fmaf(s[e >> 4][e & 15], cm[e >> 4], -mo[e >> 4]);
     } else if constexpr (kind == OP_X) {
       st.t[e] = fast_exp2(st.t[e]);
     } else {
@@ -390,7 +441,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   // l += the sum of one half's bf16 weights (two v_dot2 chains per block: their latency).  Pairs
   // are taken with whole-vector shuffles: this compiler folds word extracts from a bit-cast
   // vector wrongly.
-  auto row_sums = [&](const bf16x8 (&pb)[2][2]) {
+  auto row_sums = [&](const bf16x8 (&pb)[2][2], float isv) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float a0 = 0.f, a1 = 0.f;
@@ -401,7 +452,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 4, 5), ones2, a0, false);
         a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[qb][k2], pb[qb][k2], 6, 7), ones2, a1, false);
       }
-      l[qb] += a0 + a1;
+      if constexpr (V8) l[qb] = fmaf(a0 + a1, isv, l[qb]);  // back from s_v * P to P
+      else l[qb] += a0 + a1;
     }
   };
   auto anchor_l = [&]() { asm volatile("" ::"v"(l[0]), "v"(l[1])); };
@@ -416,11 +468,12 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       }
   };
   // P for one half without interleaving (prologue)
-  auto make_p_plain = [&](const f32x16 (&s)[2], const float (&cm)[2], bf16x8 (&pb)[2][2]) {
+  auto make_p_plain = [&](const f32x16 (&s)[2], const float (&cm)[2], const float (&mo)[2], float isv,
+                          bf16x8 (&pb)[2][2]) {
     ValuState st;
-    static_for<0, kValuOps>([&](auto kc) { valu_op(kc, st, s, cm); });
+    static_for<0, kValuOps>([&](auto kc) { valu_op(kc, st, s, cm, mo); });
     p_operands(st, pb);
-    row_sums(pb);
+    row_sums(pb, isv);
   };
 
   // One half step.  MFMAs: (if HAS_S) the scores of half kb_next from K buffer sk into s_next, and
@@ -434,8 +487,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   // address dlds + 1024 j, global base dbase), spread evenly over its MFMA regions so that the
   // memory pipeline takes them in the background instead of stalling the wave on a burst.
   auto half_step = [&](auto has_s, auto has_p, const uint8_t* sk, int kb_next, f32x16 (&s_next)[2],
-                       const uint16_t* sv, int half, const bf16x8 (&pb_in)[2][2],
-                       const f32x16 (&s_src)[2], const float (&cm)[2], bf16x8 (&pb_out)[2][2],
+                       const uint8_t* sv, int half, const bf16x8 (&pb_in)[2][2],
+                       const f32x16 (&s_src)[2], const float (&cm)[2], const float (&mo)[2], bf16x8 (&pb_out)[2][2],
                        auto ndc, const uint32_t* doff, uint32_t dlds, const uint8_t* dbase) {
     constexpr bool HS = decltype(has_s)::value, HP = decltype(has_p)::value;
     constexpr int ND = decltype(ndc)::value;
@@ -445,6 +498,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     constexpr int NVOP = NP / 2;          // V operands (each feeds both query blocks)
     KVec kop[QREGS];
     bf16x8 vop[NVOP];
+    i32x4 vraw[NVOP / 2];  // e4m3 V: one read per d block feeds its two 16-key steps
     auto load_for = [&](auto rc) {  // operands whose first use is region r
       constexpr int r = decltype(rc)::value;
       static_for<0, NKOP>([&](auto kc) {
@@ -453,11 +507,26 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       });
       static_for<0, NVOP>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        if constexpr (v_first_use(t, NS, NP) == r) vop[t] = v_op(sv, t >> 1, 2 * half + (t & 1));
+        if constexpr (V8) {
+          if constexpr ((t & 1) == 0 && v_first_use(t, NS, NP) == r) vraw[t >> 1] = v8_raw(sv, t >> 1, half);
+        } else {
+          if constexpr (v_first_use(t, NS, NP) == r) vop[t] = v_op(sv, t >> 1, 2 * half + (t & 1));
+        }
       });
+    };
+    // e4m3 V: the conversion of the operands first used in region r, issued one region earlier
+    // (the read went out LA regions earlier)
+    auto conv_for = [&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      if constexpr (V8)
+        static_for<0, NVOP>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          if constexpr ((t & 1) == 0 && v_first_use(t, NS, NP) == r) v8_cvt(vraw[t >> 1], vop[t], vop[t + 1]);
+        });
     };
     ValuState st;
     static_for<0, LA>(load_for);
+    conv_for(std::integral_constant<int, 0>());
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NR>([&](auto rc) {
       constexpr int r = decltype(rc)::value;
@@ -475,11 +544,12 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         if constexpr (((2 * dj + 1) * NR) / (2 * ND) == r) Loader::dma16(dlds + 1024 * dj, doff[dj], dbase);
       });
       if constexpr (r + LA < NR) load_for(std::integral_constant<int, r + LA>());
+      if constexpr (r + 1 < NR) conv_for(std::integral_constant<int, r + 1>());
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (HP) {
         constexpr int WS = FP8 ? 2 : 1;
         static_for<valu_ops_before(r, NS, NP, WS, kValuOps), valu_ops_before(r + 1, NS, NP, WS, kValuOps)>(
-            [&](auto kc) { valu_op(kc, st, s_src, cm); });
+            [&](auto kc) { valu_op(kc, st, s_src, cm, mo); });
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -557,6 +627,16 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     cm[0] = cq[0] * ksc;  // > 0, so scaling commutes with the max
     cm[1] = cq[1] * ksc;
   };
+  // e4m3 V: the tile's V scale, the reference shifted by log2 of it, and its inverse
+  auto v_scale_of = [&](const Desc& d) -> float {
+    if constexpr (V8) return ld_const(p.v_scale, (d.row0 / 64) * H + head);
+    else return 1.f;
+  };
+  auto set_mo = [&](float vsc, float (&mo)[2]) {
+    const float lv = log2f(vsc);
+    mo[0] = m[0] - lv;
+    mo[1] = m[1] - lv;
+  };
 
   bool fixed_m = false;  // pass 1: m already holds the true row max
   for (int pass = 0; pass < 2; ++pass) {
@@ -579,6 +659,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     float cm_cur[2];
     set_cm(k_scale_of(0, d0), cm_cur);
     float ksc_nxt = k_scale_of(1, d1);
+    float vsc_cur = v_scale_of(d0), vsc_nxt = v_scale_of(d1);
+    float mo_cur[2];  // e4m3 V only
     int nv_cur = d0.nv;
     if (wave_active) {
       f32x16 s0[2];
@@ -587,7 +669,8 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) m[qb] = pair_max(lane_max(s0[qb], s_a[qb], cm_cur[qb]));
       }
-      make_p_plain(s0, cm_cur, p_a);
+      if constexpr (V8) set_mo(vsc_cur, mo_cur);
+      make_p_plain(s0, cm_cur, V8 ? mo_cur : m, V8 ? 1.f / vsc_cur : 1.f, p_a);
     }
     wait_all_but_slot(1);
     __syncthreads();
@@ -605,22 +688,25 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       // the segment's end the descriptors repeat its last tile, so every step issues the same
       // number of (in-bounds) loads and the wait below is a constant
       constexpr int FB = (B + 2) % NBUF;
-      const bool k_ragged = d3.nv < BN, v_ragged = d2.nv < BN;  // rare: a chunk's last tile
+      // rare: a chunk's last tile (an e4m3 V block is always whole: its tail codes are 0)
+      const bool k_ragged = d3.nv < BN, v_ragged = !V8 && d2.nv < BN;
       if (k_ragged) ld.set_k(d3.nv, head, H);
       if (v_ragged) ld.set_v(d2.nv, head, H);
       const uint8_t* fkb = kpool + (size_t)d3.row0 * H * Loader::KB;
-      const uint8_t* fvb = vpool + (size_t)d2.row0 * H * 2 * D;
+      const uint8_t* fvb = Loader::v_base(vpool, d2.row0, head, H);
       const uint32_t fkl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[FB] + ld.wave_u * KI * 1024;
       const uint32_t fvl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[FB] + ld.wave_u * VI * 1024;
       // descriptors for the next step
       const Desc d4 = load_desc(j + 4);
       const float ksc_n2 = k_scale_of(j + 2, d2);
+      const float vsc_n2 = v_scale_of(d2);
       const int nv_nxt = d1.nv;
-      float cm_nxt[2];
+      float cm_nxt[2], mo_nxt[2];
       set_cm(ksc_nxt, cm_nxt);
+      if constexpr (V8) set_mo(vsc_nxt, mo_nxt);
       if (wave_active) {
         const uint8_t* sk = reinterpret_cast<const uint8_t*>(smem_k[B]);
-        const uint16_t* sv = smem_v[B];
+        const uint8_t* sv = smem_v[B];
         if (nv_cur < BN) {  // tile j is a chunk's last, partial tile
           score_drain(s_a);
           mask_half(s_a, 1, nv_cur);
@@ -628,18 +714,18 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         // A: scores of tile j+1 half 0; P.V of tile j half 0; P of tile j half 1
         f32x16 s_n0[2];
         bf16x8 p_1[2][2];
-        half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, p_1,
+        half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, V8 ? mo_cur : m, p_1,
                   std::integral_constant<int, KI>(), ld.koff, fkl, fkb);
         if (nv_nxt < BN) {
           score_drain(s_n0);
           mask_half(s_n0, 0, nv_nxt);
         }
         // B: scores of tile j+1 half 1; P.V of tile j half 1; P of tile j+1 half 0
-        half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, p_a,
+        half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, V8 ? mo_nxt : m, p_a,
                   std::integral_constant<int, VI>(), ld.voff, fvl, fvb);
         __builtin_amdgcn_sched_barrier(0);
-        row_sums(p_1);
-        row_sums(p_a);
+        row_sums(p_1, V8 ? 1.f / vsc_cur : 1.f);
+        row_sums(p_a, V8 ? 1.f / vsc_nxt : 1.f);
       } else {  // a wave without query rows still does its share of the fills
 #pragma unroll
         for (int i = 0; i < KI; ++i) Loader::dma16(fkl + 1024 * i, ld.koff[i], fkb);
@@ -650,6 +736,12 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       if (v_ragged) ld.set_v(BN, head, H);
       cm_cur[0] = cm_nxt[0];
       cm_cur[1] = cm_nxt[1];
+      if constexpr (V8) {
+        mo_cur[0] = mo_nxt[0];
+        mo_cur[1] = mo_nxt[1];
+        vsc_cur = vsc_nxt;
+        vsc_nxt = vsc_n2;
+      }
       nv_cur = nv_nxt;
       d1 = d2;
       d2 = d3;
@@ -663,18 +755,18 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     // copy O between AGPRs, and such copies cannot be ordered after the asm MFMAs that write O).
     auto last = [&](int b) {
       if (wave_active) {
-        const uint16_t* sv = smem_v[b];
+        const uint8_t* sv = smem_v[b];
         if (nv_cur < BN) {
           score_drain(s_a);
           mask_half(s_a, 1, nv_cur);
         }
         f32x16 dummy[2];
         bf16x8 p_1[2][2], p_unused[2][2];
-        half_step(std::false_type(), std::true_type(), nullptr, 0, dummy, sv, 0, p_a, s_a, cm_cur, p_1,
-                  std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
-        half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, p_unused,
-                  std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
-        row_sums(p_1);
+        half_step(std::false_type(), std::true_type(), nullptr, 0, dummy, sv, 0, p_a, s_a, cm_cur, V8 ? mo_cur : m,
+                  p_1, std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
+        half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, V8 ? mo_cur : m,
+                  p_unused, std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
+        row_sums(p_1, V8 ? 1.f / vsc_cur : 1.f);
       }
     };
     for (int j = 0;;) {
@@ -814,11 +906,11 @@ __device__ bool gate_item(const FwdParams& p, const int32_t* items, int item, in
 
 // Persistent workgroup: runs the segments [ranges[2w], ranges[2w+1]) of the uploaded schedule.
 // GATED: every item first passes gate_item.
-template <int D, bool FP8, bool OUT_F32, bool GATED>
+template <int D, bool FP8, bool OUT_F32, bool GATED, bool V8 = false>
 __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
-  using Loader = TileLoader<D, FP8>;
+  using Loader = TileLoader<D, FP8, V8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem_k[NBUF][BN * Loader::KB];
-  __shared__ __attribute__((aligned(16))) uint16_t smem_v[NBUF][BN * D];
+  __shared__ __attribute__((aligned(16))) uint8_t smem_v[NBUF][Loader::VBYTES];
   __shared__ int redo_flags[NTHR / 64];
   const int32_t* hdr = p.blob;
   if (ld_const(hdr, H_NONCE_LO) != (int32_t)p.nonce_lo || ld_const(hdr, H_NONCE_HI) != (int32_t)p.nonce_hi) return;
@@ -833,7 +925,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
     if constexpr (GATED) {
       if (!gate_item(p, items, item, &gate_decision)) continue;
     }
-    run_segment<D, FP8, OUT_F32, GATED>(p, items, item, ld_const(segs, sg * kSegInts + 1),
+    run_segment<D, FP8, OUT_F32, GATED, V8>(p, items, item, ld_const(segs, sg * kSegInts + 1),
                                  ld_const(segs, sg * kSegInts + 2), ld_const(segs, sg * kSegInts + 3), tiles, smem_k, smem_v, redo_flags);
   }
 }
@@ -937,6 +1029,13 @@ hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream
     if (p.gate_flags) hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, false>), dim3(grid), dim3(NTHR), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fp8kv(const FwdParams& p, int head_dim, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, false, true>), dim3(grid), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 

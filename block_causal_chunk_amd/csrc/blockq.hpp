@@ -23,11 +23,12 @@ struct BlockLayout {
 // the block (NaN ignored), scale = amax/448 and multiplier 448/amax (both correctly rounded),
 // codes = RNE e4m3 of v * multiplier clamped to [-448, 448] (NaN kept); amax == 0 gives scale 1.
 // Row r of the codes goes to x8 + r * row_stride; the scale to *scale_out.
+// The block's scale and multiplier (amax over rows < nrows, NaN ignored; amax == 0 gives 1, 1).
 template <int D>
-__device__ __forceinline__ void quantize_regs(const float (&v)[BlockLayout<D>::ITER][8], int nrows, size_t row_stride,
-                                              uint8_t* __restrict__ x8, float* __restrict__ scale_out) {
+__device__ __forceinline__ void block_scale(const float (&v)[BlockLayout<D>::ITER][8], int nrows, float& scale,
+                                            float& mult) {
   using L = BlockLayout<D>;
-  const int g = threadIdx.x % L::GPR, rsub = threadIdx.x / L::GPR;
+  const int rsub = threadIdx.x / L::GPR;
   float amax = 0.f;
 #pragma unroll
   for (int it = 0; it < L::ITER; ++it) {
@@ -52,11 +53,21 @@ __device__ __forceinline__ void quantize_regs(const float (&v)[BlockLayout<D>::I
 #pragma unroll
   for (int w = 1; w < 4; ++w) amax = (wmax[w] > amax) ? wmax[w] : amax;
   __syncthreads();  // wmax is reused by the next block of this workgroup
-  float scale = 1.f, mult = 1.f;
+  scale = 1.f;
+  mult = 1.f;
   if (amax > 0.f) {
     scale = __fdiv_rn(amax, 448.f);
     mult = __fdiv_rn(448.f, amax);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void quantize_regs(const float (&v)[BlockLayout<D>::ITER][8], int nrows, size_t row_stride,
+                                              uint8_t* __restrict__ x8, float* __restrict__ scale_out) {
+  using L = BlockLayout<D>;
+  const int g = threadIdx.x % L::GPR, rsub = threadIdx.x / L::GPR;
+  float scale, mult;
+  block_scale<D>(v, nrows, scale, mult);
   if (threadIdx.x == 0) *scale_out = scale;
 #pragma unroll
   for (int it = 0; it < L::ITER; ++it) {

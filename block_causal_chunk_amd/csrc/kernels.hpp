@@ -14,6 +14,8 @@ struct FwdParams {
   const float* q_scale;    // [nqb, H]                      (fp8 path)
   const uint8_t* k8;       // e4m3 pool                     (fp8 path)
   const float* k_scale;    // [pool_rows / 64, H]           (fp8 path)
+  const uint8_t* v8;       // e4m3 V pool [pool_rows / 64, H, D, 64] (e4m3 K/V storage)
+  const float* v_scale;    // [pool_rows / 64, H]           (e4m3 K/V storage)
   void* out;               // bf16 or fp32 [Lq, H, D]
   float* lse;              // [H, Lq] or nullptr
   const int32_t* blob;     // uploaded work list (device)
@@ -81,6 +83,9 @@ struct RopeParams {
 
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s);
 hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream_t s);
+hipError_t launch_attn_fp8kv(const FwdParams& p, int head_dim, int grid, hipStream_t s);
+hipError_t launch_quantize_v_fp8(const uint16_t* v, int64_t rows, int32_t heads, int32_t head_dim, uint8_t* v8,
+                                 float* scales, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, int head_dim, bool out_f32, int groups, hipStream_t s);
 hipError_t launch_publish(const PublishParams& p, int64_t tokens, hipStream_t s);
 // flags[chunk] = generation, release-ordered after everything before it on the stream

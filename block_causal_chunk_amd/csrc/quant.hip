@@ -49,7 +49,67 @@ __global__ __launch_bounds__(256) void publish_e4m3_kernel(PublishFp8Params p) {
   }
 }
 
+// e4m3 V pool for e4m3 K/V storage: workgroup (64-row block, head) quantizes the block exactly as
+// quantize_e4m3_kernel (amax over the finite values, the same scale and RNE codes), except that a
+// NaN value is padding (a slot past a chunk's end) and gets code 0, and writes the codes
+// transposed, [channel][64 key slots], into the block's 64*D bytes of v8 (layout [rows/64, H, D,
+// 64]).  Within each 32-key half the slots hold the 8-key groups in the order 0, 2, 1, 3, so that
+// one 16-byte read of a channel gives a lane of the attention's P.V the keys of both its 16-key
+// steps.  The transpose goes through LDS so that the stores are whole 16-byte granules.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_v8_kernel(const uint16_t* __restrict__ x, int heads,
+                                                          uint8_t* __restrict__ v8, float* __restrict__ scales) {
+  using L = BlockLayout<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * 64];
+  const int64_t blk = blockIdx.x / heads;
+  const int head = blockIdx.x % heads;
+  const int g = threadIdx.x % L::GPR, rsub = threadIdx.x / L::GPR;
+  const uint16_t* src = x + ((size_t)blk * 64 * heads + head) * D;
+  float v[L::ITER][8];
+#pragma unroll
+  for (int it = 0; it < L::ITER; ++it)
+    unpack8(*reinterpret_cast<const uint4*>(src + (size_t)(it * L::RPI + rsub) * heads * D + g * 8), v[it]);
+  float scale, mult;
+  block_scale<D>(v, 64, scale, mult);
+  if (threadIdx.x == 0) scales[blk * heads + head] = scale;
+#pragma unroll
+  for (int it = 0; it < L::ITER; ++it) {
+    const int r = it * L::RPI + rsub;
+    const int grp = (r >> 3) & 3;
+    const int slot = (r & ~31) | ((grp == 1 ? 2 : grp == 2 ? 1 : grp) << 3) | (r & 7);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float t = __fmul_rn(v[it][j], mult);
+      t = (t > 448.f) ? 448.f : t;
+      t = (t < -448.f) ? -448.f : t;
+      y[j] = (v[it][j] == v[it][j]) ? t : 0.f;  // NaN: padding, code 0
+    }
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      tile[(8 * g + j) * 64 + slot] = (uint8_t)(((j < 4 ? (uint32_t)w0 : (uint32_t)w1) >> (8 * (j & 3))) & 0xff);
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(v8 + ((size_t)blk * heads + head) * (size_t)(64 * D));
+  for (int i = threadIdx.x; i < D * 4; i += 256) dst[i] = reinterpret_cast<const uint4*>(tile)[i];
+}
+
 }  // namespace
+
+hipError_t launch_quantize_v_fp8(const uint16_t* v, int64_t rows, int32_t heads, int32_t head_dim, uint8_t* v8,
+                                 float* scales, hipStream_t s) {
+  const int64_t grid = rows / 64 * heads;
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(quantize_v8_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, v, heads, v8, scales);
+  else
+    hipLaunchKernelGGL(quantize_v8_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, v, heads, v8, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int32_t heads, int32_t head_dim, uint8_t* x8,
                                float* scales, hipStream_t s) {

@@ -85,6 +85,9 @@ WORKLOADS = {
     # 14B-shaped chunk task for the fp8 Q.K^T path
     "wan14b_fp8": dict(k=5, H=40, d=128, tokens=[4680] * 4, queries=[3], page=256,
                        shuffle=True, spare=8, dtype="bf16"),
+    # the same task with K and V both stored as e4m3 (same seed, so the same values)
+    "wan14b_fp8kv": dict(k=5, H=40, d=128, tokens=[4680] * 4, queries=[3], page=256,
+                         shuffle=True, spare=8, dtype="bf16"),
 }
 
 # Scaled-down variants that the CPU oracle finishes in well under a second.

@@ -215,6 +215,39 @@ wfattn_status wfattn_fwd_fp8_marked(const wfattn_plan_t* plan, const uint8_t* q8
 wfattn_status wfattn_quantize_fp8(const void* x_bf16, int64_t rows, int32_t heads,
                                   int32_t head_dim, uint8_t* x8, float* scales, void* stream);
 
+/* ---- e4m3 K/V storage ---------------------------------------------------------------------
+ * K and V both stored as e4m3 (the project page's "03 - End-to-end KV transport", "Precision"
+ * panel: FP8 K/V halves the bytes moved; here it halves the K/V bytes the attention gathers).
+ * The e4m3 V pool has its own layout, [num_pages * page_size / 64, H, d, 64]: per (64-key block,
+ * head) the block's d x 64 codes stored channel by channel, and inside each 32-key half of a
+ * channel the 8-key groups in the order 0, 2, 1, 3; codes of slots past a chunk's last token are
+ * 0.  One fp32 scale per (64-key block, head), layout as k_scale.  v_pool value of key u of a block
+ * = decode(code) * scale. */
+
+/* e4m3 V pool from a bf16 pool: v_bf16 [rows, heads, head_dim] (rows = num_pages * page_size, a
+ * multiple of 64) -> v8 (the layout above) and scales [rows/64, heads].  Per (64-row block, head)
+ * exactly the rule of wfattn_quantize_fp8 (amax over the finite values, scale = amax/448, RNE
+ * codes), except that a NaN value -- a padding slot -- gets code 0.
+ * Errors: NULL, UNSUPPORTED (head_dim not 64/128, alignment), RANGE (rows < 0 or not a multiple
+ * of 64, heads < 1), DEVICE. */
+wfattn_status wfattn_quantize_v_fp8(const void* v_bf16, int64_t rows, int32_t heads,
+                                    int32_t head_dim, uint8_t* v8, float* scales, void* stream);
+
+/* Forward with e4m3 Q.K^T (as wfattn_fwd_fp8) and e4m3 V (v8_pool, v_scale: the layout above).
+ * Each V code converts exactly to bf16 and P.V runs as a bf16 MFMA with fp32 accumulation; the V
+ * block scale is folded into the softmax weights (s_v * P), and the normaliser sums the weights
+ * that multiply V.  ws: wfattn_workspace_bytes(plan, WFATTN_WS_FP8).  Errors as wfattn_fwd_fp8. */
+wfattn_status wfattn_fwd_fp8kv(const wfattn_plan_t* plan, const uint8_t* q8, const float* q_scale,
+                               const uint8_t* k8_pool, const float* k_scale, const uint8_t* v8_pool,
+                               const float* v_scale, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+/* Measurement aid: wfattn_fwd_fp8kv with the event of wfattn_fwd_marked. */
+wfattn_status wfattn_fwd_fp8kv_marked(const wfattn_plan_t* plan, const uint8_t* q8,
+                                      const float* q_scale, const uint8_t* k8_pool,
+                                      const float* k_scale, const uint8_t* v8_pool,
+                                      const float* v_scale, void* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* attn_done_event, void* stream);
+
 /* ---- producer side: publish a chunk's K/V, and a forward gated on it ------------------------
  * The producers write each chunk's keys and values straight into the slots the consumer reads
  * (project page, "03 - End-to-end KV transport", panel "03 - Layout"), and a consumer uses a

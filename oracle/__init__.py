@@ -228,6 +228,56 @@ def dequantize_e4m3(x8, scales) -> np.ndarray:
     return y
 
 
+# Slot of key k inside its 64-key block of the e4m3 V pool: within each 32-key half the 8-key
+# groups are stored in the order 0, 2, 1, 3 (a layout choice of the e4m3 K/V storage, written out
+# here from its statement, not derived from the GPU code).
+_V8_GROUP_SLOT = (0, 2, 1, 3)
+
+
+def v8_slot(key: int) -> int:
+    half, grp, j = key // 32, (key // 8) % 4, key % 8
+    return 32 * half + 8 * _V8_GROUP_SLOT[grp] + j
+
+
+def quantize_v8(x):
+    """e4m3 V pool of the e4m3 K/V storage (project page, "03 - End-to-end KV transport",
+    "Precision" panel: FP8 K/V) from pool rows x [rows, H, d] (rows a multiple of 64; NaN marks
+    padding slots): the block quantizer's codes and scales (``quantize_e4m3``: one scale per 64
+    rows and head), a NaN value's code set to 0, then each (64-row block, head) laid out channel by
+    channel with key k of the block at slot ``v8_slot(k)``.
+    Returns (v8 uint8 [rows/64, H, d, 64], scales f32 [rows/64, H])."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    xf = np.ascontiguousarray(x, dtype=np.float32)
+    rows, H, d = xf.shape
+    if rows % 64:
+        raise ValueError("rows must be a multiple of 64")
+    x8, sc = quantize_e4m3(xf)
+    x8[np.isnan(xf)] = 0
+    blocks = x8.reshape(rows // 64, 64, H, d).transpose(0, 2, 3, 1)  # [block, H, d, key]
+    out = np.empty(blocks.shape, np.uint8)
+    for key in range(64):
+        out[..., v8_slot(key)] = blocks[..., key]
+    return out, sc
+
+
+def dequantize_v8(v8, scales) -> np.ndarray:
+    """Values of an e4m3 V pool in the layout of ``quantize_v8``, in pool row order [rows, H, d],
+    fp64: decode(code) * scale of its (64-row block, head)."""
+    v8 = np.asarray(v8, dtype=np.uint8)
+    nb, H, d, _ = v8.shape
+    lut = np.array([lib().oracle_e4m3_decode(c) for c in range(256)], np.float64)
+    keys = np.empty((nb, H, d, 64), np.float64)
+    for key in range(64):
+        keys[..., key] = lut[v8[..., v8_slot(key)]]
+    keys *= np.asarray(scales, np.float64)[:, :, None, None]
+    return np.ascontiguousarray(keys.transpose(0, 3, 1, 2).reshape(nb * 64, H, d))
+
+
 def merge_lse(o_parts, lse_parts):
     """Softmax over a union of disjoint key sets from the parts' normalised outputs and LSEs:
     out = sum_k exp(lse_k - lse) o_k, lse = log sum_k exp(lse_k) (an identity of the softmax; the

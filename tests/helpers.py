@@ -120,3 +120,12 @@ def check_lse(got, ref, sumw2, what=""):
     assert r.size < 64 or float(r.mean()) <= 1.5, (what, "lse spread (mean)", float(r.mean()), float(r.max()))
     assert float(r.max()) <= 8.0, (what, "lse spread (max)", float(r.mean()), float(r.max()))
     return float(r.mean()), float(r.max())
+
+
+def head_slice(table, q, k_pool, v_pool, heads):
+    """The same call restricted to `heads` (attention is independent per head): a table with
+    len(heads) heads and the matching slices of Q and the pools."""
+    t = table.copy()
+    t.num_heads = len(heads)
+    hs = list(heads)
+    return t, q[:, hs].contiguous(), k_pool[:, :, hs].contiguous(), v_pool[:, :, hs].contiguous()

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 from block_causal_chunk_amd.inputs import fill_case, make_case, make_table
-from helpers import check_bf16, check_lse, check_contract_bf16, check_fp8_contract, f64, sample_rows, stats, to_dev
+from helpers import (check_bf16, check_contract_bf16, check_fp8_contract, check_lse, f64, head_slice, sample_rows,
+                     stats, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,15 +94,6 @@ def test_merge_of_more_than_four_pieces(B, O, io):
     ref, ref_lse, ref_w2 = O.attn_rows(c.table, c.q, c.k_pool, c.v_pool, want_sumw2=True)
     check_bf16(f64(out), ref, "wave_round split 7")
     check_lse(f64(lse).T, ref_lse, ref_w2)
-
-
-def head_slice(table, q, k_pool, v_pool, heads):
-    """The same call restricted to `heads` (attention is independent per head): a table with
-    len(heads) heads and the matching slices of Q and the pools."""
-    t = table.copy()
-    t.num_heads = len(heads)
-    hs = list(heads)
-    return t, q[:, hs].contiguous(), k_pool[:, :, hs].contiguous(), v_pool[:, :, hs].contiguous()
 
 
 @pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])

@@ -594,3 +594,37 @@ def test_pins_detect_plausible_mistakes(oracle_lib):
     bad.softmax_scale = 1.0 / 128  # 1/d instead of 1/sqrt(d)
     o = oracle_lib.attn_rows(bad, c.q, c.k_pool, c.v_pool)[0]
     assert np.abs(o - ref).max() > 1e-3
+
+
+# ---------------------------------------------------------------- e4m3 V pool (e4m3 K/V storage)
+def test_v8_slot_order_is_the_stated_permutation(oracle_lib):
+    """Keys 0-7 -> slots 0-7, 8-15 -> 16-23, 16-23 -> 8-15, 24-31 -> 24-31, the same in the upper
+    half; a bijection on 0..63."""
+    slots = [oracle_lib.v8_slot(k) for k in range(64)]
+    assert slots[:8] == list(range(8)) and slots[8:16] == list(range(16, 24))
+    assert slots[16:24] == list(range(8, 16)) and slots[24:32] == list(range(24, 32))
+    assert slots[32:] == [32 + s for s in slots[:32]]
+    assert sorted(slots) == list(range(64))
+
+
+def test_v8_quantizer_against_the_row_quantizer(oracle_lib):
+    """Every finite value's code and scale are those of the row-layout block quantizer (P8), placed
+    at [block, head, channel, slot(key)]; NaN padding gets code 0; dequantizing gives back
+    decode * scale in row order (0 at padding)."""
+    rng = np.random.default_rng(29)
+    rows, H, d = 192, 3, 16
+    x = (rng.standard_normal((rows, H, d)) * rng.choice([0.1, 1.0, 30.0], size=(rows, 1, 1))).astype(np.float32)
+    x[150:] = np.nan  # a chunk's last block, partly padding
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    v8, sc = oracle_lib.quantize_v8(x)
+    x8, sc_rows = oracle_lib.quantize_e4m3(x)
+    assert np.array_equal(sc, sc_rows)
+    for r in range(rows):
+        b, key = divmod(r, 64)
+        for h in range(H):
+            for c in range(d):
+                want = 0 if np.isnan(x[r, h, c]) else x8[r, h, c]
+                assert v8[b, h, c, oracle_lib.v8_slot(key)] == want
+    y = oracle_lib.dequantize_v8(v8, sc)
+    ref = np.nan_to_num(oracle_lib.dequantize_e4m3(x8, sc_rows), nan=0.0)
+    assert np.array_equal(y, ref)
