@@ -23,7 +23,7 @@ EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_work
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
             "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish", "wfattn_fwd_marked",
             "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated", "wfattn_fwd_noalloc", "wfattn_quantize_v_fp8",
-            "wfattn_fwd_fp8kv", "wfattn_fwd_fp8kv_marked"]
+            "wfattn_fwd_fp8kv", "wfattn_fwd_fp8kv_marked", "wfattn_device_geometry"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 WFATTN_NOALLOC_MAX_BYTES = 64 << 20
 
@@ -46,7 +46,8 @@ class ChunkTableC(ctypes.Structure):
 
 class OptsC(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("order_ties", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
+                ("order_ties", ctypes.c_int32), ("num_cus", ctypes.c_int32), ("num_xcds", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32)]
 
 
 _lib = None
@@ -93,6 +94,8 @@ def lib():
         L.wfattn_rope_publish.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz,
                                           vp]
         L.wfattn_rope_publish.restype = i32
+        L.wfattn_device_geometry.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.wfattn_device_geometry.restype = i32
         L.wfattn_quantize_v_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.wfattn_quantize_v_fp8.restype = i32
         L.wfattn_fwd_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -176,13 +179,27 @@ def make_table_c(table):
     return c, arrs
 
 
-def wfattn_plan(table, split_k: int = 0, xcd_remap: int = 0, order_ties: int = 0) -> Plan:
+def wfattn_plan(table, split_k: int = 0, xcd_remap: int = 0, order_ties: int = 0, num_cus: int = 0,
+                num_xcds: int = 0) -> Plan:
     c, keep = make_table_c(table)
-    o = OptsC(int(split_k), int(xcd_remap), int(order_ties), 0)
+    o = OptsC(int(split_k), int(xcd_remap), int(order_ties), int(num_cus), int(num_xcds), 0, 0)
     h = ctypes.c_void_p()
     _check(lib().wfattn_plan(ctypes.byref(c), ctypes.byref(o), ctypes.byref(h)), "wfattn_plan")
     del keep
     return Plan(h.value)
+
+
+_GEOMETRY = {}
+
+
+def device_geometry(device: int):
+    """(compute units, XCDs) of HIP device `device`, read once per device."""
+    if device not in _GEOMETRY:
+        cus, xcds = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().wfattn_device_geometry(int(device), ctypes.byref(cus), ctypes.byref(xcds)),
+               "wfattn_device_geometry")
+        _GEOMETRY[device] = (int(cus.value), int(xcds.value))
+    return _GEOMETRY[device]
 
 
 def wfattn_plan_upload(plan: Plan, ws, stream=None):
@@ -290,7 +307,10 @@ class Attention:
                  stream=None, order_ties: int = 0):
         import torch
         self.table = table
-        self.plan = wfattn_plan(table, split_k=split_k, xcd_remap=xcd_remap, order_ties=order_ties)
+        dev = torch.device(device)
+        cus, xcds = device_geometry(dev.index if dev.index is not None else torch.cuda.current_device())
+        self.plan = wfattn_plan(table, split_k=split_k, xcd_remap=xcd_remap, order_ties=order_ties, num_cus=cus,
+                                num_xcds=xcds)
         self.mode = mode
         nbytes = self.plan.workspace_bytes(mode)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

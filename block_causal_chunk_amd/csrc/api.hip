@@ -79,10 +79,13 @@ wfattn_status fwd_impl(const wfattn_plan_t* plan, wfattn_dtype dtype, const void
     uint16_t* sk = reinterpret_cast<uint16_t*>(w + P->stage_k_off);
     uint16_t* sv = reinterpret_cast<uint16_t*>(w + P->stage_v_off);
     const int64_t qn = P->lq * P->num_heads * P->head_dim;
-    const int64_t pn = P->pool_rows * P->num_heads * P->head_dim;
+    const int64_t row_elems = static_cast<int64_t>(P->num_heads) * P->head_dim;
+    const int32_t* tiles = fp.blob + P->off_tiles;  // the uploaded tile list; visible tiles first
     if (launch_f32_to_bf16(static_cast<const float*>(q), sq, qn, s) != hipSuccess ||
-        launch_f32_to_bf16(static_cast<const float*>(k_pool), sk, pn, s) != hipSuccess ||
-        launch_f32_to_bf16(static_cast<const float*>(v_pool), sv, pn, s) != hipSuccess)
+        launch_f32_tiles_to_bf16(static_cast<const float*>(k_pool), sk, tiles, P->n_vis_tiles, row_elems, s) !=
+            hipSuccess ||
+        launch_f32_tiles_to_bf16(static_cast<const float*>(v_pool), sv, tiles, P->n_vis_tiles, row_elems, s) !=
+            hipSuccess)
       return WFATTN_ERR_DEVICE;
     fp.q = sq;
     fp.k = sk;
@@ -311,6 +314,18 @@ extern "C" wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t 
   return launch_rope_publish(rp, tokens, P->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
              ? WFATTN_OK
              : WFATTN_ERR_DEVICE;
+}
+
+extern "C" wfattn_status wfattn_device_geometry(int32_t device, int32_t* num_cus, int32_t* num_xcds) {
+  if (!num_cus || !num_xcds) return WFATTN_ERR_NULL;
+  int cus = 0, xcc = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+    return WFATTN_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, device) != hipSuccess || xcc < 1 || cus % xcc != 0)
+    xcc = 1;  // unknown: treat the device as one L2 domain
+  *num_cus = cus;
+  *num_xcds = xcc;
+  return WFATTN_OK;
 }
 
 extern "C" wfattn_status wfattn_quantize_v_fp8(const void* v_bf16, int64_t rows, int32_t heads, int32_t head_dim,

@@ -1004,7 +1004,28 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
   }
 }
 
+// fp32 -> bf16 staging of the pool rows some query can see: block i converts key tile i of the
+// plan's tile list (its valid rows, row_elems = H * d values each); other rows are never read.
+__global__ __launch_bounds__(256) void f32_tiles_to_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out,
+                                                                const int32_t* __restrict__ tiles, int64_t row_elems) {
+  const int64_t base = (int64_t)tiles[2 * blockIdx.x] * row_elems;
+  const int64_t n4 = (int64_t)tiles[2 * blockIdx.x + 1] * row_elems / 4;
+  const float4* src = reinterpret_cast<const float4*>(in + base);
+  uint2* dst = reinterpret_cast<uint2*>(out + base);
+  for (int64_t i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = src[i];
+    dst[i] = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_f32_tiles_to_bf16(const float* in, uint16_t* out, const int32_t* tiles, int n_tiles, int64_t row_elems,
+                                    hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(f32_tiles_to_bf16_kernel, dim3((unsigned)n_tiles), dim3(256), 0, s, in, out, tiles, row_elems);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;

@@ -93,6 +93,9 @@ hipError_t launch_flag(uint32_t* flags, int32_t chunk, uint32_t generation, hipS
 hipError_t launch_publish_fp8(const PublishFp8Params& p, int64_t tokens, int32_t head_dim, hipStream_t s);
 hipError_t launch_rope_publish(const RopeParams& p, int64_t tokens, int32_t head_dim, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+// the rows of key tiles 0 .. n_tiles-1 of a plan's tile list (device), row_elems values per row
+hipError_t launch_f32_tiles_to_bf16(const float* in, uint16_t* out, const int32_t* tiles, int n_tiles, int64_t row_elems,
+                                    hipStream_t s);
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int32_t heads, int32_t head_dim,
                                uint8_t* x8, float* scales, hipStream_t s);
 

@@ -74,7 +74,7 @@ wfattn_status validate(const wfattn_chunk_table* t, bool ties) {
   return WFATTN_OK;
 }
 
-constexpr int kCUs = 256;      // MI355X compute units; workgroup w starts on XCD w % 8
+constexpr int kCUs = 256;      // MI355X compute units (the default); workgroup w starts on XCD w % 8
 constexpr int kXCDs = 8;
 constexpr int kSegOverhead = 3; // a segment's Q load + epilogue, in key-tile units
 constexpr int kMinSplit = 8;    // never cut a segment shorter than this many key tiles
@@ -113,9 +113,13 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
   if (!table || !plan_out) return WFATTN_ERR_NULL;
   wfattn_opts o{};
   if (opts) o = *opts;
-  if (o.order_ties < 0 || o.order_ties > 1 || o.reserved1 != 0 || o.split_k < 0 || o.split_k > 64 ||
-      o.xcd_remap < -1 || o.xcd_remap > 1)
+  if (o.order_ties < 0 || o.order_ties > 1 || o.split_k < 0 || o.split_k > 64 || o.xcd_remap < -1 ||
+      o.xcd_remap > 1 || o.num_cus < 0 || o.num_cus > 4096 || o.num_xcds < 0 ||
+      (o.block_m != 0 && o.block_m != kBlockM) || (o.block_n != 0 && o.block_n != kBlockN))
     return WFATTN_ERR_UNSUPPORTED;
+  const int32_t n_cus = o.num_cus ? o.num_cus : kCUs;
+  const int32_t n_xcds = o.num_xcds ? o.num_xcds : (o.num_cus ? 1 : kXCDs);
+  if (n_xcds > n_cus || n_cus % n_xcds != 0) return WFATTN_ERR_UNSUPPORTED;
   wfattn_status st = validate(table, o.order_ties == 1);
   if (st != WFATTN_OK) return st;
 
@@ -135,6 +139,9 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
     P.scale = table->softmax_scale > 0.f ? table->softmax_scale
                                          : static_cast<float>(1.0 / std::sqrt((double)table->head_dim));
     P.xcd_remap = (o.xcd_remap == -1) ? 0 : 1;
+    P.n_cus = n_cus;
+    P.n_xcds = n_xcds;
+    const int CU = n_cus, XCD = n_xcds;
 
     // Key tiles of all chunks, clean -> noisy (chunks of equal order by index); prefix_end[c] =
     // tiles up to and including the last chunk whose order is not above c's, so the visible keys
@@ -167,6 +174,8 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
         last_rank[by_order[r]] = last_rank[by_order[r + 1]];
       }
     P.n_tiles = static_cast<int32_t>(tiles.size() / kTileInts);
+    for (int i = 0; i < table->num_query_chunks; ++i)
+      P.n_vis_tiles = std::max(P.n_vis_tiles, prefix_end[table->query_chunks[i]]);
 
     // Items: (query chunk, query tile of up to kBlockM rows, head) with the whole visible prefix.
     std::vector<Item> items;
@@ -204,25 +213,25 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
                              static_cast<int32_t>(static_cast<int64_t>(nt) * (j + 1) / k), -1});
       }
       const int n_segs = static_cast<int>(segs.size());
-      if (n_segs <= kCUs && P.xcd_remap) {
+      if (n_segs <= CU && P.xcd_remap) {
         // one segment per workgroup: the head-major segment list laid out XCD by XCD, so the
         // workgroups of one XCD walk the same heads' keys side by side and share them in L2
-        per_wg.assign(kCUs, {});
+        per_wg.assign(CU, {});
         int64_t worst = 0;
         for (int L = 0; L < n_segs; ++L) {
-          per_wg[(L / (kCUs / kXCDs)) + kXCDs * (L % (kCUs / kXCDs))].push_back(L);
+          per_wg[(L / (CU / XCD)) + XCD * (L % (CU / XCD))].push_back(L);
           worst = std::max<int64_t>(worst, segs[L].kt1 - segs[L].kt0 + kSegOverhead);
         }
         return worst;
       }
-      const int bins = std::min<int>(kCUs, n_segs);
+      const int bins = std::min<int>(CU, n_segs);
       return lpt(segs, bins, per_wg);
     };
-    // Stream-K: the head-major list of key tiles cut into kCUs ranges of equal cost; logical
-    // range L runs on workgroup (L / 32) + 8 * (L % 32), so the 32 workgroups of one XCD share
-    // a contiguous run of heads and hence their K/V in that XCD's L2.
+    // Stream-K: the head-major list of key tiles cut into CU ranges of equal cost; logical range L
+    // runs on workgroup (L / (CU/XCD)) + XCD * (L % (CU/XCD)) (on MI355X (L / 32) + 8 * (L % 32)),
+    // so the workgroups of one XCD share a contiguous run of heads and hence their K/V in its L2.
     auto stream_k = [&]() {
-      const int G = kCUs;
+      const int G = CU;
       segs.clear();
       per_wg.assign(G, {});
       // item i owns tiles [first[i], first[i] + n_tiles) of one global axis; logical range L is
@@ -243,7 +252,7 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
       cut[G] = total;
       int i = 0;
       for (int L = 0; L < G; ++L) {
-        const int w = P.xcd_remap ? (L / (G / kXCDs)) + kXCDs * (L % (G / kXCDs)) : L;
+        const int w = P.xcd_remap ? (L / (G / XCD)) + XCD * (L % (G / XCD)) : L;
         while (i < n_items && first[i + 1] <= cut[L]) ++i;
         for (int j = i; j < n_items && first[j] < cut[L + 1]; ++j) {
           const int64_t a = std::max(cut[L], first[j]), b = std::min(cut[L + 1], first[j + 1]);
@@ -465,4 +474,4 @@ extern "C" const char* wfattn_status_str(wfattn_status s) {
   return "unknown status";
 }
 
-extern "C" int32_t wfattn_abi_version(void) { return 2; }
+extern "C" int32_t wfattn_abi_version(void) { return 3; }

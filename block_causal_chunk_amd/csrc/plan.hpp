@@ -54,6 +54,8 @@ struct Plan {
   float scale = 0.f;        // resolved softmax scale
   // schedule
   int32_t block_m = kBlockM, block_n = kBlockN, max_parts = 1, xcd_remap = 1;
+  int32_t n_cus = 256, n_xcds = 8;  // the device the schedule spreads over
+  int32_t n_vis_tiles = 0;          // key tiles some query chunk sees (a prefix of the tile list)
   int32_t n_items = 0, n_tiles = 0, n_groups = 0, n_partials = 0, n_segs = 0, n_wgs = 0;
   std::vector<int32_t> blob;  // header, items, segments, ranges, key tiles, merge groups
   size_t off_items = 0, off_segs = 0, off_ranges = 0, off_tiles = 0, off_groups = 0;  // int32 offsets

@@ -109,15 +109,26 @@ typedef struct wfattn_opts {
                       /* bidirectional window of Rolling Forcing, Wave Forcing project page,   */
                       /* "01 - The design gap", column "A - Live frontier"), while every       */
                       /* cleaner order stays one-way.  Other values: UNSUPPORTED.              */
-  int32_t reserved1; /* must be 0 */
+  int32_t num_cus;   /* compute units the persistent schedule spreads over: 0 = 256 (a whole      */
+                     /* MI355X); else 1..4096, e.g. hipDeviceProp_t.multiProcessorCount of a     */
+                     /* partitioned device (wfattn_device_geometry reads both counts)            */
+  int32_t num_xcds;  /* L2 domains (XCDs) those CUs are dealt to round-robin by workgroup index:  */
+                     /* 0 = 8 when num_cus is 0, else 1; must divide the CU count                 */
+  int32_t block_m;   /* query rows per work item: 0 or 256 (the kernels' query tile; fixed)       */
+  int32_t block_n;   /* keys per tile: 0 or 64 (the kernels' key tile; fixed).  Other values of  */
+                     /* either: UNSUPPORTED                                                      */
 } wfattn_opts;
 
 typedef struct wfattn_plan_s wfattn_plan_t; /* opaque, host memory only, immutable once built   */
 
 /* Validate `table` and build the work list: for each query chunk its visible key prefix in
  * clean -> noisy order, query tiles that never cross a chunk, key tiles that never cross a page,
- * and a schedule over the CUs.  Host only, no HIP call.  The plan owns copies of everything it
- * needs; free it with wfattn_plan_free.  Errors: NULL, INVALID, RANGE, UNSUPPORTED, NOMEM. */
+ * and a schedule over the CUs.  The visible set of query chunk a is every chunk b with
+ * chunk_order[b] <= chunk_order[a] (Wave Forcing project page, "01 - The design gap", column "C -
+ * Directed live frontier" and "Key observation"), and it is read where the producers put it
+ * (same page, "03 - End-to-end KV transport", "Layout" panel), so the plan only lists page rows.
+ * Host only, no HIP call.  The plan owns copies of everything it needs; free it with
+ * wfattn_plan_free.  Errors: NULL, INVALID, RANGE, UNSUPPORTED (an option out of range), NOMEM. */
 wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfattn_opts* opts /* NULL ok */,
                           wfattn_plan_t** plan_out);
 void wfattn_plan_free(wfattn_plan_t* plan); /* NULL ok */
@@ -157,7 +168,12 @@ wfattn_status wfattn_plan_upload(const wfattn_plan_t* plan, void* ws, size_t ws_
 wfattn_status wfattn_plan_describe(const wfattn_plan_t* plan, int32_t what, int32_t* buf,
                                    size_t cap, size_t* n);
 
-/* bf16 (or fp32 I/O) forward.  q, k_pool, v_pool, out in `dtype`; lse NULL or [H, Lq] fp32.
+/* bf16 (or fp32 I/O) forward: out = softmax(scale q k^T) v over each query row's visible keys
+ * (the block-causal chunk mask of the project page, "01 - The design gap", column C: full inside a
+ * chunk, every earlier and cleaner chunk, never a later and noisier one), with the pages read in
+ * place ("03 - End-to-end KV transport", "Layout" panel).
+ * q, k_pool, v_pool, out in `dtype`; lse NULL or [H, Lq] fp32.  fp32 I/O converts Q and only
+ * the pool rows some query can see to bf16 in the workspace.
  * ws must hold wfattn_workspace_bytes(plan, dtype == WFATTN_FP32 ? WFATTN_WS_FP32 :
  * WFATTN_WS_BF16) bytes and have been filled by wfattn_plan_upload from this plan.  Device
  * pointers must be 16-byte aligned (ws 256-byte).  Padding slots of the pools are never read.
@@ -169,7 +185,9 @@ wfattn_status wfattn_fwd(const wfattn_plan_t* plan, wfattn_dtype dtype, const vo
                          const void* k_pool, const void* v_pool, void* out, float* lse, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* Forward with e4m3 (OCP E4M3FN) Q.K^T: q8 [Lq,H,d] and k8_pool [num_pages,page_size,H,d] are
+/* The forward of wfattn_fwd (same mask, same pages) with the scores from FP8 operands (the
+ * reduced-precision K/V of the project page's "03 - End-to-end KV transport", "Precision" panel):
+ * e4m3 (OCP E4M3FN) Q.K^T: q8 [Lq,H,d] and k8_pool [num_pages,page_size,H,d] are
  * e4m3 codes with one fp32 scale per (64-row block, head) (value = decode(code) * scale, the
  * layout of q_scale / k_scale is given at the top of this file); v_pool and out are bf16.
  * Scores are accumulated in fp32 and scaled once per block pair; P.V runs in bf16.
@@ -347,7 +365,12 @@ wfattn_status wfattn_fwd_noalloc(const wfattn_plan_t* plan, wfattn_dtype dtype, 
 /* Static string naming a status. */
 const char* wfattn_status_str(wfattn_status status);
 
-/* ABI version of this header: 2 (2 gave wfattn_opts.order_ties its meaning; it had to be 0). */
+/* The compute units and XCDs of HIP device `device`, for wfattn_opts.num_cus / num_xcds
+ * (hipDeviceProp_t.multiProcessorCount and the device's XCC count).  Errors: NULL, DEVICE. */
+wfattn_status wfattn_device_geometry(int32_t device, int32_t* num_cus, int32_t* num_xcds);
+
+/* ABI version of this header: 3 (2 gave wfattn_opts.order_ties its meaning; 3 replaced the
+ * reserved word of wfattn_opts with num_cus and added num_xcds, block_m and block_n). */
 int32_t wfattn_abi_version(void);
 
 #ifdef __cplusplus

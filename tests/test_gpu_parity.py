@@ -991,6 +991,15 @@ def test_fp8_full_size_all_rows(B, O):
     check_lse(f64(lse).T[:, heads], ref_dq_lse, ref_dq_w2, "wan14b_fp8 (dequantized oracle)")
 
 
+def test_device_geometry(B):
+    """The device the planner spreads over: every CU of the GPU, dealt round-robin to its XCDs (an
+    unpartitioned MI355X reports 256 CUs in 8 XCDs)."""
+    cus, xcds = B.device_geometry(torch.cuda.current_device())
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    print(f"[case] device geometry {cus} CUs, {xcds} XCDs ({props.name})", flush=True)
+    assert cus == props.multi_processor_count and xcds >= 1 and cus % xcds == 0
+
+
 def test_measurement_probes():
     """The benchmark's probes: the copy kernel copies exactly (an odd number of granules, a grid
     capped below the size), and the exp-rate kernel's chains stay finite in [0.5, 1] per value."""

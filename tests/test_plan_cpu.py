@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(B):
     L = B.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wfattn_abi_version() == 2
+    assert L.wfattn_abi_version() == 3
     for s in range(8):
         assert B.status_str(s) and B.status_str(s) != "unknown status"
 
@@ -64,7 +64,8 @@ def test_probe_library_exports_and_rejects_bad_arguments(B):
 
 def _plan_status(B, t, **opts):
     c, keep = B.make_table_c(t)
-    o = B.OptsC(opts.get("split_k", 0), opts.get("xcd_remap", 0), opts.get("order_ties", 0), opts.get("r1", 0))
+    o = B.OptsC(opts.get("split_k", 0), opts.get("xcd_remap", 0), opts.get("order_ties", 0), opts.get("num_cus", 0),
+                opts.get("num_xcds", 0), opts.get("block_m", 0), opts.get("block_n", 0))
     h = ctypes.c_void_p()
     st = B.lib().wfattn_plan(ctypes.byref(c), ctypes.byref(o), ctypes.byref(h))
     if st == 0:
@@ -114,7 +115,15 @@ def test_plan_errors(B):
     assert _plan_status(B, t) == B.WFATTN_ERR_UNSUPPORTED
     assert _plan_status(B, _base(), order_ties=2) == B.WFATTN_ERR_UNSUPPORTED
     assert _plan_status(B, _base(), order_ties=-1) == B.WFATTN_ERR_UNSUPPORTED
-    assert _plan_status(B, _base(), r1=1) == B.WFATTN_ERR_UNSUPPORTED
+    # the kernels' tiles are fixed: block_m / block_n accept 0 or those values only
+    assert _plan_status(B, _base(), block_m=256, block_n=64) == B.WFATTN_OK
+    assert _plan_status(B, _base(), block_m=128) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), block_n=32) == B.WFATTN_ERR_UNSUPPORTED
+    # device geometry: the XCD count must divide the CU count
+    assert _plan_status(B, _base(), num_cus=84, num_xcds=8) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), num_cus=-1) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), num_cus=4097) == B.WFATTN_ERR_UNSUPPORTED
+    assert _plan_status(B, _base(), num_cus=64, num_xcds=2) == B.WFATTN_OK
     # ties only where asked for; an order outside [0, num_chunks) stays invalid either way
     t = _base()
     t.chunk_order = np.array([0, 1, 1], np.int32)
@@ -262,7 +271,7 @@ def _check_schedule(B, t, **kw):
     segs = plan.describe(4).reshape(-1, 4)
     ranges = plan.describe(5).reshape(-1, 2)
     assert items.shape[0] == n_items and tiles.shape[0] == n_tiles and groups.shape[0] == n_groups
-    assert segs.shape[0] == n_segs and ranges.shape[0] == n_wgs and 1 <= n_wgs <= 256
+    assert segs.shape[0] == n_segs and ranges.shape[0] == n_wgs and 1 <= n_wgs <= (kw.get("num_cus") or 256)
     # workgroup ranges partition the segment list in order
     assert ranges[0, 0] == 0 and ranges[-1, 1] == n_segs
     assert (ranges[1:, 0] == ranges[:-1, 1]).all() and (ranges[:, 1] >= ranges[:, 0]).all()
@@ -418,3 +427,20 @@ def test_noalloc_forward_checks_before_any_device_call(B):
     assert L.wfattn_fwd_noalloc(plan.handle, 7, fake, fake, fake, fake, None, None) == B.WFATTN_ERR_UNSUPPORTED
     assert L.wfattn_fwd_noalloc(plan.handle, B.WFATTN_BF16, fake + 8, fake, fake, fake, None, None) == \
         B.WFATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("cus,xcds", [(32, 1), (128, 4), (80, 0), (304, 8)])
+def test_schedule_on_a_partitioned_or_other_device(B, cus, xcds):
+    """A device with another CU / XCD count (a compute partition of the chip, another part):
+    every workgroup index stays below the CU count, the mask is still covered exactly once, and
+    the work is balanced over those CUs."""
+    from block_causal_chunk_amd.inputs import WORKLOADS
+    w = WORKLOADS["wan13b_task"]
+    t = make_table(w["tokens"], list(range(len(w["tokens"]))), w["queries"], w["page"], w["H"], w["d"],
+                   shuffle_rng=np.random.default_rng(0), spare=w["spare"])
+    plan, items, tiles = _check_schedule(B, t, num_cus=cus, num_xcds=xcds)
+    segs = plan.describe(4).reshape(-1, 4)
+    ranges = plan.describe(5).reshape(-1, 2)
+    assert ranges.shape[0] <= cus
+    load = np.array([sum(int(segs[s][2] - segs[s][1]) + 3 for s in range(a, b)) for a, b in ranges])
+    assert load.max() <= 1.12 * load.mean() + 16, (load.max(), load.mean())
