@@ -148,6 +148,63 @@ def rope_publish(B, att, t, k_pool, k8_pool, k_scale, v, reps: int = 20):
                              "hbm_frac": round(nbytes / (ms * 1e-3) / 8e12, 4)}}
 
 
+def qkv_fused(B, att, t, k_pool, v, reps: int = 20):
+    """Outside the timed steps: the producer's QKV projection of the (first) query chunk with the
+    pre-attention epilogue fused (wfattn_qkv_rope_publish: x [tokens, H*d] . W [H*d, 3*H*d] on the
+    matrix cores, rotation, bf16 Q out, K and V into the pages), against the same work in two
+    passes: torch's matmul (the vendor GEMM) writing the [tokens, 3, H, d] projection, then
+    wfattn_rope_publish reading it back.  Both timed with HIP events, blocks alternated."""
+    import numpy as np
+    import torch
+    H, d = t.num_heads, t.head_dim
+    a = int(t.query_chunks[0])
+    n = int(t.chunk_tokens[a])
+    hid = H * d
+    dev = v.device
+    x = torch.randn((n, hid), device=dev).to(torch.bfloat16)
+    w = (torch.randn((hid, 3 * hid), device=dev) / hid ** 0.5).to(torch.bfloat16)
+    th = torch.rand((n, d // 2), device=dev) * 6.283185307179586
+    cos_t, sin_t = torch.cos(th), torch.sin(th)
+    q_out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    kp, vp = k_pool.clone(), v.clone()
+    qkv = torch.empty((n, 3 * hid), dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        B.wfattn_qkv_rope_publish(att.plan, a, x, w, cos_t, sin_t, q_out, None, None, kp, None, None, vp, None, 0,
+                                  att.ws)
+
+    def two_pass():
+        torch.matmul(x, w, out=qkv)
+        B.wfattn_rope_publish(att.plan, a, qkv, cos_t, sin_t, q_out, None, None, kp, None, None, vp, None, 0, att.ws)
+
+    def gemm_only():
+        torch.matmul(x, w, out=qkv)
+
+    for f in (fused, two_pass):
+        for _ in range(5):
+            f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = {"fused": [], "two_pass": [], "gemm_only": []}
+    for _ in range(3):
+        for name, f in (("fused", fused), ("two_pass", two_pass), ("gemm_only", gemm_only)):
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / reps)
+    ms = {k: float(np.median(v)) for k, v in times.items()}
+    flop = 2.0 * n * hid * 3 * hid
+    inter = n * 3 * hid * 2  # the [tokens, 3, H, d] bf16 projection, written then read back
+    return {"qkv_rope_publish": {"chunk_tokens": n, "hidden": hid, "fused_ms": round(ms["fused"], 4),
+                                 "fused_tflops": round(flop / (ms["fused"] * 1e-3) / 1e12, 1),
+                                 "fused_frac_of_bf16_peak": round(flop / (ms["fused"] * 1e-3) / 1e12 / PEAK_BF16, 4),
+                                 "two_pass_ms": round(ms["two_pass"], 4),
+                                 "vendor_gemm_alone_ms": round(ms["gemm_only"], 4),
+                                 "intermediate_bytes_avoided": 2 * inter}}
+
+
 def publish_fp8(B, att, t, q, k8, ks, v, reps: int = 20):
     """Outside the timed steps: wfattn_publish_kv_fp8 of the query chunk (K quantized to e4m3 per
     64-token block and head into the K8 pool, V copied), HBM-bound: 2 B read + 1 B written per K
@@ -565,6 +622,8 @@ def main():
     if not (f32 or args.no_extras):
         extra = publish_fp8(B, att, t, q, k8, ks, v) if fp8 else publish_and_gate(B, att, t, q, k, v)
         extra.update(rope_publish(B, att, t, None if fp8 else k, k8 if fp8 else None, ks if fp8 else None, v))
+        if not fp8:
+            extra.update(qkv_fused(B, att, t, k, v))
     exp_peak = exp_peak_per_s()
     p50 = r["p50_ms"]
     flops = effective_flops(t)

@@ -23,7 +23,7 @@ EXPORTED = ["wfattn_plan", "wfattn_plan_free", "wfattn_query_rows", "wfattn_work
             "wfattn_quantize_fp8", "wfattn_status_str", "wfattn_abi_version", "wfattn_publish_kv",
             "wfattn_fwd_gated", "wfattn_publish_kv_fp8", "wfattn_rope_publish", "wfattn_fwd_marked",
             "wfattn_fwd_fp8_marked", "wfattn_fwd_fp8_gated", "wfattn_fwd_noalloc", "wfattn_quantize_v_fp8",
-            "wfattn_fwd_fp8kv", "wfattn_fwd_fp8kv_marked", "wfattn_device_geometry"]
+            "wfattn_fwd_fp8kv", "wfattn_fwd_fp8kv_marked", "wfattn_device_geometry", "wfattn_qkv_rope_publish"]
 WFATTN_GATE_SPIN_MAX = 1 << 20
 WFATTN_NOALLOC_MAX_BYTES = 64 << 20
 
@@ -94,6 +94,9 @@ def lib():
         L.wfattn_rope_publish.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz,
                                           vp]
         L.wfattn_rope_publish.restype = i32
+        L.wfattn_qkv_rope_publish.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_uint32, vp, sz, vp]
+        L.wfattn_qkv_rope_publish.restype = i32
         L.wfattn_device_geometry.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.wfattn_device_geometry.restype = i32
         L.wfattn_quantize_v_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
@@ -238,6 +241,15 @@ def wfattn_rope_publish(plan: Plan, chunk: int, qkv, cos_t, sin_t, q_out, q8, q_
                                      _ptr(q8), _ptr(q_scale), _ptr(k_pool), _ptr(k8_pool), _ptr(k_scale),
                                      _ptr(v_pool), _ptr(flags), int(generation) & 0xffffffff, _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "wfattn_rope_publish")
+
+
+def wfattn_qkv_rope_publish(plan: Plan, chunk: int, x, w, cos_t, sin_t, q_out, q8, q_scale, k_pool, k8_pool,
+                            k_scale, v_pool, flags, generation: int, ws, stream=None):
+    _check(lib().wfattn_qkv_rope_publish(plan.handle, int(chunk), _ptr(x), _ptr(w), int(x.shape[1]), _ptr(cos_t),
+                                         _ptr(sin_t), _ptr(q_out), _ptr(q8), _ptr(q_scale), _ptr(k_pool),
+                                         _ptr(k8_pool), _ptr(k_scale), _ptr(v_pool), _ptr(flags),
+                                         int(generation) & 0xffffffff, _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "wfattn_qkv_rope_publish")
 
 
 def wfattn_fwd_gated(plan: Plan, q, k_pool, v_pool, out, lse, ws, flags, need, spin_limit: int, gate_status,

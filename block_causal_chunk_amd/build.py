@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwfattn.so")
-SOURCES = ["plan.cpp", "api.hip", "attn_fwd.hip", "quant.hip", "publish.hip"]
+SOURCES = ["plan.cpp", "api.hip", "attn_fwd.hip", "quant.hip", "publish.hip", "qkv.hip"]
 PROBE_LIB = os.path.join(HERE, "libwfprobe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"

@@ -316,6 +316,53 @@ extern "C" wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t 
              : WFATTN_ERR_DEVICE;
 }
 
+extern "C" wfattn_status wfattn_qkv_rope_publish(const wfattn_plan_t* plan, int32_t chunk, const void* x, const void* w,
+                                                 int32_t hidden, const float* cos_t, const float* sin_t, void* q_out,
+                                                 uint8_t* q8, float* q_scale, void* k_pool, uint8_t* k8_pool,
+                                                 float* k_scale, void* v_pool, uint32_t* flags, uint32_t generation,
+                                                 const void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !x || !w || !cos_t || !sin_t || !v_pool) return WFATTN_ERR_NULL;
+  if (!k_pool == !k8_pool) return WFATTN_ERR_INVALID;  // exactly one form of K
+  if ((k8_pool && !k_scale) || (q8 && !q_scale)) return WFATTN_ERR_NULL;
+  if (!plan_ok(plan)) return WFATTN_ERR_INVALID;
+  const Plan* P = as_plan(plan);
+  if (chunk < 0 || chunk >= P->num_chunks) return WFATTN_ERR_INVALID;
+  if (hidden < 64 || hidden % 64 != 0) return WFATTN_ERR_UNSUPPORTED;
+  // the kernel addresses x with 32-bit byte offsets
+  if (static_cast<int64_t>(P->blob[P->off_chunks + static_cast<size_t>(chunk) * kChunkInts + 1]) * hidden * 2 >
+      INT32_MAX)
+    return WFATTN_ERR_RANGE;
+  if (!ws) return WFATTN_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(cos_t, 4) || !aligned(sin_t, 4) || !aligned(q_out, 16) ||
+      !aligned(q8, 16) || !aligned(q_scale, 4) || !aligned(k_pool, 16) || !aligned(k8_pool, 16) ||
+      !aligned(k_scale, 4) || !aligned(v_pool, 16) || !aligned(flags, 4) || !aligned(ws, 256))
+    return WFATTN_ERR_UNSUPPORTED;
+  if (ws_bytes < P->ws_base_bytes) return WFATTN_ERR_WORKSPACE;
+  QkvParams qp{};
+  qp.x = static_cast<const uint16_t*>(x);
+  qp.w = static_cast<const uint16_t*>(w);
+  qp.tokens = P->blob[P->off_chunks + static_cast<size_t>(chunk) * kChunkInts + 1];
+  qp.hidden = hidden;
+  qp.cos_t = cos_t;
+  qp.sin_t = sin_t;
+  qp.q_out = static_cast<uint16_t*>(q_out);
+  qp.q8 = q8;
+  qp.q_scale = q_scale;
+  qp.k_pool = static_cast<uint16_t*>(k_pool);
+  qp.k8_pool = k8_pool;
+  qp.k_scale = k_scale;
+  qp.v_pool = static_cast<uint16_t*>(v_pool);
+  qp.blob = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + P->ws_blob);
+  qp.chunk = chunk;
+  qp.heads = P->num_heads;
+  qp.nonce_lo = static_cast<uint32_t>(P->nonce & 0xffffffffu);
+  qp.nonce_hi = static_cast<uint32_t>(P->nonce >> 32);
+  qp.flags = flags;
+  qp.generation = generation;
+  return launch_qkv_rope_publish(qp, P->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess ? WFATTN_OK
+                                                                                                  : WFATTN_ERR_DEVICE;
+}
+
 extern "C" wfattn_status wfattn_device_geometry(int32_t device, int32_t* num_cus, int32_t* num_xcds) {
   if (!num_cus || !num_xcds) return WFATTN_ERR_NULL;
   int cus = 0, xcc = 0;

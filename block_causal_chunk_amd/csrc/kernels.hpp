@@ -81,6 +81,28 @@ struct RopeParams {
   uint32_t generation;
 };
 
+struct QkvParams {
+  const uint16_t* x;       // bf16 [tokens, hidden]: the chunk's hidden states
+  const uint16_t* w;       // bf16 [hidden, 3 * H * D]: columns (role, head, channel), role q, k, v
+  int32_t tokens;
+  int32_t hidden;          // a multiple of 64
+  const float* cos_t;      // [tokens, D/2]
+  const float* sin_t;      // [tokens, D/2]
+  uint16_t* q_out;         // bf16 [tokens, H, D] or nullptr
+  uint8_t* q8;             // e4m3 [tokens, H, D] or nullptr
+  float* q_scale;          // [ceil(tokens/64), H]
+  uint16_t* k_pool;        // bf16 pool, or nullptr when k8_pool is set
+  uint8_t* k8_pool;        // e4m3 pool, or nullptr
+  float* k_scale;          // [pool_rows / 64, H]
+  uint16_t* v_pool;        // bf16 pool
+  const int32_t* blob;
+  int32_t chunk;
+  int32_t heads;
+  uint32_t nonce_lo, nonce_hi;
+  uint32_t* flags;
+  uint32_t generation;
+};
+
 hipError_t launch_attn_bf16(const FwdParams& p, int head_dim, bool out_f32, int grid, hipStream_t s);
 hipError_t launch_attn_fp8(const FwdParams& p, int head_dim, int grid, hipStream_t s);
 hipError_t launch_attn_fp8kv(const FwdParams& p, int head_dim, int grid, hipStream_t s);
@@ -92,6 +114,7 @@ hipError_t launch_publish(const PublishParams& p, int64_t tokens, hipStream_t s)
 hipError_t launch_flag(uint32_t* flags, int32_t chunk, uint32_t generation, hipStream_t s);
 hipError_t launch_publish_fp8(const PublishFp8Params& p, int64_t tokens, int32_t head_dim, hipStream_t s);
 hipError_t launch_rope_publish(const RopeParams& p, int64_t tokens, int32_t head_dim, hipStream_t s);
+hipError_t launch_qkv_rope_publish(const QkvParams& p, int32_t head_dim, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 // the rows of key tiles 0 .. n_tiles-1 of a plan's tile list (device), row_elems values per row
 hipError_t launch_f32_tiles_to_bf16(const float* in, uint16_t* out, const int32_t* tiles, int n_tiles, int64_t row_elems,

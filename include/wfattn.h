@@ -322,6 +322,23 @@ wfattn_status wfattn_rope_publish(const wfattn_plan_t* plan, int32_t chunk, cons
                                   void* v_pool, uint32_t* flags, uint32_t generation,
                                   const void* ws, size_t ws_bytes, void* stream);
 
+/* The producer's QKV projection with the epilogue of wfattn_rope_publish fused into it: publish
+ * K/V right after projecting them, at every layer (KipQuest paper page, "The deep dive"), without
+ * the [chunk_tokens, 3, H, d] projection output going through memory.  x: bf16 [chunk_tokens,
+ * hidden] (the chunk's hidden states, hidden a multiple of 64); w: bf16 [hidden, 3*H*d], columns
+ * ordered (q|k|v, head, channel), so qkv = x . w is the qkv input of wfattn_rope_publish.  The
+ * product is accumulated in fp32 on the matrix cores; every other step, output and argument is
+ * that of wfattn_rope_publish (rotation of q and k on the fp32 products, bf16 rounding, e4m3 of
+ * the bf16 values, page placement, flag).
+ * Errors: as wfattn_rope_publish, plus UNSUPPORTED (hidden not a positive multiple of 64), RANGE
+ * (x larger than 2 GiB). */
+wfattn_status wfattn_qkv_rope_publish(const wfattn_plan_t* plan, int32_t chunk, const void* x,
+                                      const void* w, int32_t hidden, const float* cos_t,
+                                      const float* sin_t, void* q_out, uint8_t* q8, float* q_scale,
+                                      void* k_pool, uint8_t* k8_pool, float* k_scale, void* v_pool,
+                                      uint32_t* flags, uint32_t generation, const void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* Upper bound of spin_limit in wfattn_fwd_gated: one poll is followed by a sleep of about 4000
  * clocks, so a gate gives up after about 2 s at most. */
 #define WFATTN_GATE_SPIN_MAX (1 << 20)

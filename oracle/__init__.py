@@ -163,6 +163,14 @@ def rotate_pairs(x, cos_t, sin_t):
     return out
 
 
+def qkv_project(x, w, heads: int, head_dim: int):
+    """The QKV projection in fp64: x [tokens, hidden] times w [hidden, 3*H*d] (columns ordered
+    (q|k|v, head, channel)), a plain matrix product, as [tokens, 3, H, d] float64.  The producer
+    computes it right before publishing K/V (KipQuest paper page, "The deep dive")."""
+    xd, wd = _f64(x), _f64(w)
+    return (xd @ wd).reshape(xd.shape[0], 3, int(heads), int(head_dim))
+
+
 def attn_masked(q, k, v, allowed, scale: float, nthreads: int = 0):
     """Softmax attention by its definition with an explicit 0/1 mask, one head: q [nq, d], k/v
     [nk, d], allowed [nq, nk] bool.  The pins feed it masks built independently of the chunk

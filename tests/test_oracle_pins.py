@@ -628,3 +628,20 @@ def test_v8_quantizer_against_the_row_quantizer(oracle_lib):
     y = oracle_lib.dequantize_v8(v8, sc)
     ref = np.nan_to_num(oracle_lib.dequantize_e4m3(x8, sc_rows), nan=0.0)
     assert np.array_equal(y, ref)
+
+
+# ---------------------------------------------------------------- QKV projection
+def test_qkv_projection_brute_force(oracle_lib):
+    """qkv_project against the sum written out with Python loops, and its (role, head, channel)
+    column order."""
+    rng = np.random.default_rng(31)
+    n, hid, H, d = 3, 5, 2, 4
+    x = rng.standard_normal((n, hid))
+    w = rng.standard_normal((hid, 3 * H * d))
+    y = oracle_lib.qkv_project(x, w, H, d)
+    for i in range(n):
+        for r in range(3):
+            for h in range(H):
+                for c in range(d):
+                    col = (r * H + h) * d + c
+                    assert abs(y[i, r, h, c] - sum(x[i, k] * w[k, col] for k in range(hid))) <= 1e-12
