@@ -16,7 +16,7 @@ FwdParams base_params(const Plan* P, void* ws) {
   FwdParams fp{};
   char* w = static_cast<char*>(ws);
   fp.blob = reinterpret_cast<const int32_t*>(w + P->ws_blob);
-  fp.part_o = reinterpret_cast<float*>(w + P->ws_part_o);
+  fp.part_o = reinterpret_cast<uint16_t*>(w + P->ws_part_o);
   fp.part_lse = reinterpret_cast<float*>(w + P->ws_part_lse);
   fp.H = P->num_heads;
   fp.lq = static_cast<int32_t>(P->lq);

@@ -824,6 +824,23 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     const int r = 64 * wave + 32 * qb + l32;
     const float lt = pair_sum(l[qb]);
     const float inv = 1.f / lt;
+    // A split-K partial is stored as fp16 times 2^pexp, one exponent per row, chosen so that the
+    // row's largest |value| lands in [2^14, 2^15): the full 11-bit significand for it, and no
+    // overflow whatever the magnitude of V.
+    int pexp = 0;
+    if (slot >= 0) {
+      float mx = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(o[qb][cb][i]));
+      mx = pair_max(mx) * inv;  // lanes l and l ^ 32 hold the two halves of one row
+      if (mx > 0.f && mx < INFINITY) {
+        int e;
+        frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+        pexp = e - 15;
+      }
+    }
     if (r >= q_rows) continue;
     // m is log2 of the reference exp(scale * s); lse = m * ln(2) + ln(l)
     const float lse_val = m[qb] * 0.6931471805599453f + logf(lt);
@@ -845,16 +862,18 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         }
       if (p.lse && hi == 0) p.lse[(size_t)head * p.lq + q_row0 + r] = lse_val;
     } else {
-      float* po = p.part_o + ((size_t)slot * BM + r) * D;
+      uint16_t* po = p.part_o + ((size_t)slot * BM + r) * D;
+      auto sc = [&](float x) { return ldexpf(x * inv, -pexp); };  // exact power-of-two step
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d0 = 32 * cb + 8 * g4 + 4 * hi;
-          *reinterpret_cast<float4*>(po + d0) = make_float4(o[qb][cb][4 * g4] * inv, o[qb][cb][4 * g4 + 1] * inv,
-                                                            o[qb][cb][4 * g4 + 2] * inv, o[qb][cb][4 * g4 + 3] * inv);
+          *reinterpret_cast<uint2*>(po + d0) = make_uint2(pack2_f16(sc(o[qb][cb][4 * g4]), sc(o[qb][cb][4 * g4 + 1])),
+                                                          pack2_f16(sc(o[qb][cb][4 * g4 + 2]), sc(o[qb][cb][4 * g4 + 3])));
         }
-      if (hi == 0) p.part_lse[(size_t)slot * BM + r] = lse_val;
+      if (hi == 0)
+        *reinterpret_cast<float2*>(p.part_lse + 2 * ((size_t)slot * BM + r)) = make_float2(lse_val, __int_as_float(pexp));
     }
   }
 }
@@ -930,8 +949,9 @@ __global__ __launch_bounds__(NTHR, 1) void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-// Merge of split key ranges: out = sum_k exp(lse_k - lse) * O_k, lse = log sum_k exp(lse_k).  One
-// thread per (row, 8 channels); a block covers 256 / (D/8) rows of one merge group.  The pieces are
+// Merge of split key ranges: out = sum_k exp(lse_k - lse) * O_k, lse = log sum_k exp(lse_k), where
+// O_k is piece k's fp16 row times 2^(its row exponent), the power of two folded into the piece's
+// weight.  One thread per (row, 8 channels); a block covers 256 / (D/8) rows of one merge group.  The pieces are
 // taken in batches of kMergeBatch whose loads (lse and O alike) are all issued before any is used,
 // so a batch costs one memory round trip; a later batch rescales what the earlier ones summed to
 // its new running maximum.
@@ -953,17 +973,19 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < parts; k0 += kMergeBatch) {
     float lk[kMergeBatch];
-    float4 ok[kMergeBatch][2];
+    int ek[kMergeBatch];
+    f16x8 ok[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       lk[j] = -INFINITY;
-      ok[j][0] = ok[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      ek[j] = 0;
+      ok[j] = f16x8{};
       if (k0 + j < parts) {
         const size_t row = (size_t)(slot0 + k0 + j) * BM + r;
-        lk[j] = p.part_lse[row];
-        const float4* src = reinterpret_cast<const float4*>(p.part_o + row * D + 8 * d8);
-        ok[j][0] = src[0];
-        ok[j][1] = src[1];
+        const float2 le = *reinterpret_cast<const float2*>(p.part_lse + 2 * row);
+        lk[j] = le.x;
+        ek[j] = __float_as_int(le.y);
+        ok[j] = *reinterpret_cast<const f16x8*>(p.part_o + row * D + 8 * d8);
       }
     }
     float mn = mx;
@@ -978,8 +1000,9 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
     for (int j = 0; j < kMergeBatch; ++j) {
       const float w = expf(lk[j] - mn);
       z += w;
-      acc[0] += w * ok[j][0].x; acc[1] += w * ok[j][0].y; acc[2] += w * ok[j][0].z; acc[3] += w * ok[j][0].w;
-      acc[4] += w * ok[j][1].x; acc[5] += w * ok[j][1].y; acc[6] += w * ok[j][1].z; acc[7] += w * ok[j][1].w;
+      const float wo = ldexpf(w, ek[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wo * (float)ok[j][e];
     }
     mx = mn;
   }

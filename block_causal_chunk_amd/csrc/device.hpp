@@ -14,6 +14,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #define WF_LDS __attribute__((address_space(3)))
 
@@ -91,6 +92,14 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // v_cvt_pk_bf16_f32
+}
+
+// Pack 2 fp32 into fp16x2 with round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack2_f16(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
 }  // namespace wfattn

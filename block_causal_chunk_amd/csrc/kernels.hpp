@@ -19,8 +19,8 @@ struct FwdParams {
   void* out;               // bf16 or fp32 [Lq, H, D]
   float* lse;              // [H, Lq] or nullptr
   const int32_t* blob;     // uploaded work list (device)
-  float* part_o;           // [n_partials, BM, D]
-  float* part_lse;         // [n_partials, BM]
+  uint16_t* part_o;        // fp16 [n_partials, BM, D]: row r holds O_r * 2^-e_r
+  float* part_lse;         // [n_partials, BM, 2]: the row's LSE, then e_r (int32 bits)
   int32_t H;
   int32_t lq;
   float c;                 // softmax scale * log2(e)

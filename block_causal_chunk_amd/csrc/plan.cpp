@@ -366,10 +366,12 @@ extern "C" wfattn_status wfattn_plan(const wfattn_chunk_table* table, const wfat
     const size_t D = static_cast<size_t>(P.head_dim);
     P.ws_blob = 0;
     size_t off = align_up(P.blob.size() * sizeof(int32_t), 256);
+    // split-K partials: O as fp16 with a power-of-two exponent per row; per row, the LSE and the
+    // exponent side by side
     P.ws_part_o = off;
-    off = align_up(off + static_cast<size_t>(P.n_partials) * kBlockM * D * sizeof(float), 256);
+    off = align_up(off + static_cast<size_t>(P.n_partials) * kBlockM * D * sizeof(uint16_t), 256);
     P.ws_part_lse = off;
-    off = align_up(off + static_cast<size_t>(P.n_partials) * kBlockM * sizeof(float), 256);
+    off = align_up(off + static_cast<size_t>(P.n_partials) * kBlockM * 2 * sizeof(float), 256);
     P.ws_base_bytes = off;
     const size_t pool_elems = static_cast<size_t>(P.pool_rows) * P.num_heads * D;
     const size_t q_elems = static_cast<size_t>(P.lq) * P.num_heads * D;
