@@ -66,7 +66,7 @@ def gather_bytes(table, k_bytes: int, v_bytes: int = 2) -> tuple:
 
 def kernel_src_hash() -> str:
     h = hashlib.sha256()
-    for f in ["attn_fwd.hip", "device.hpp", "plan.cpp", "plan.hpp"]:
+    for f in ["attn_fwd.hip", "device.hpp", "kernels.hpp", "plan.cpp", "plan.hpp"]:
         h.update(open(os.path.join(ROOT, "block_causal_chunk_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

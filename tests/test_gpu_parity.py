@@ -96,6 +96,26 @@ def test_merge_of_more_than_four_pieces(B, O, io):
     check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
+@pytest.mark.parametrize("k", [20, -60])
+def test_split_partials_keep_any_magnitude(B, O, k):
+    """Split-K partials are fp16 with one power-of-two exponent per row, so no |V| overflows them
+    (fp16 alone would at 2^16): V scaled by 2^k (exact in bf16) gives every output times exactly
+    2^k and the same LSE, split or not, and the scaled call matches the oracle."""
+    c = make_case("wan13b_task", small=True)
+    c2 = type(c)(c.name, c.table, c.io_dtype, c.q, c.k_pool, c.v_pool * 2.0 ** k)
+    for split in (1, 0, 3):  # the last, compared with the oracle below, goes through partials
+        print(f"[case] V scaled by 2^{k}, split_k={split}", flush=True)
+        o1, l1, _ = run(B, c, split_k=split)
+        o2, l2, att = run(B, c2, split_k=split)
+        if split == 3:
+            assert int(att.plan.describe(0)[3]) > 0  # the call does go through partials
+        assert torch.equal(o2.float(), o1.float() * 2.0 ** k), (k, split)
+        assert torch.equal(l1, l2)
+    ref, ref_lse, ref_w2 = O.attn_rows(c2.table, c2.q, c2.k_pool, c2.v_pool, want_sumw2=True)
+    check_bf16(f64(o2), ref, f"V x 2^{k}", contract=False)  # outputs of scale 2^k: relative gates
+    check_lse(f64(l2).T, ref_lse, ref_w2)
+
+
 @pytest.mark.parametrize("name", ["wan13b_task", "wave_round", "long_rollout"])
 def test_full_size_all_rows(B, O, name):
     """Full size, in the configuration bench.py times.  wan13b_task: every row of every head
