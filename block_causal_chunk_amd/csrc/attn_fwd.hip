@@ -108,10 +108,11 @@ struct TileLoader {
       return (uint32_t)((src * H + head) * 2 * D + g * 16);
     }
   }
-  // e4m3 V tile in LDS: row c (a channel) holds 64 key bytes as 4 granules; physical granule p
-  // holds logical granule p ^ ((c / 2) mod 4), so the 8 lanes of one 128-byte read phase
-  // (channels c .. c+7, one logical granule) touch 8 distinct 16-byte bank groups.
-  __device__ __forceinline__ static int v8swz(int c, int g) { return g ^ ((c >> 1) & 3); }
+  // e4m3 V tile in LDS: row c (a channel) holds 64 key bytes as 4 granules, four rows per 256-byte
+  // line of the 64 banks; physical granule p holds logical granule p ^ ((c / 4) mod 4), so the 16
+  // lanes of one ds_read_b128 phase (channels c .. c+15, one logical granule) touch 16 distinct
+  // 16-byte bank groups.
+  __device__ __forceinline__ static int v8swz(int c, int g) { return g ^ ((c >> 2) & 3); }
   // first byte of the V tile whose first key is pool row row0
   __device__ __forceinline__ static const uint8_t* v_base(const uint8_t* vpool, int row0, int head, int H) {
     if constexpr (V8) return vpool + ((size_t)(row0 / 64) * H + head) * (size_t)(64 * D);
