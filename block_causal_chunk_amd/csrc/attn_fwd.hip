@@ -10,8 +10,8 @@
 // "03 - End-to-end KV transport", "Layout" panel).
 //
 // Data flow (4 waves, 64 query rows each, as two 32-row MFMA blocks):
-//   K, V tiles [64 x d] : global -> LDS with global_load_lds_dwordx4, a ring of three buffers
-//                         filled two tiles ahead of their use
+//   K, V tiles [64 x d] : global -> LDS with global_load_lds_dwordx4, a ring of four buffers;
+//                         each pair of key steps fills the two buffers the previous pair read
 //   S^T = K . Q^T       : v_mfma_f32_32x32x16_bf16, K rows read from LDS in a bit-swapped order
 //                         so each lane ends up owning 16 keys of one query
 //   softmax             : P = exp2(S * c - m) in fp32 against a fixed per-row reference m
@@ -38,7 +38,7 @@ namespace {
 constexpr int BM = kBlockM;  // 256 query rows per workgroup
 constexpr int BN = kBlockN;  // 64 keys per tile
 constexpr int NTHR = 256;    // 4 waves of 64
-constexpr int NBUF = 3;      // LDS ring depth (tiles)
+constexpr int NBUF = 4;      // LDS ring depth (tiles)
 
 // Row of the K tile that lane row r of the S^T A-operand reads: bits 2 and 3 swapped.  With it,
 // accumulator register i of lane l holds key 16*(i/8) + 8*(l/32) + i%8 of the 32-key block.
@@ -484,15 +484,17 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   constexpr int NP = D / 8;           // P.V MFMAs per half: 2 blocks x D/32 x 2 k-steps
   constexpr int LA = 3;               // operand loads run this many MFMA regions ahead
   //
-  // It also issues ND tile fills (global -> LDS, 1 KB per wave each, offsets doff, LDS byte
-  // address dlds + 1024 j, global base dbase), spread evenly over its MFMA regions so that the
-  // memory pipeline takes them in the background instead of stalling the wave on a burst.
+  // It also issues two groups of tile fills (global -> LDS, 1 KB per wave each; group g: ND_g loads,
+  // offsets doff_g, LDS byte address dlds_g + 1024 j, global base dbase_g), spread evenly over its
+  // MFMA regions so that the memory pipeline takes them in the background instead of stalling the
+  // wave on a burst.
   auto half_step = [&](auto has_s, auto has_p, const uint8_t* sk, int kb_next, f32x16 (&s_next)[2],
                        const uint8_t* sv, int half, const bf16x8 (&pb_in)[2][2],
                        const f32x16 (&s_src)[2], const float (&cm)[2], const float (&mo)[2], bf16x8 (&pb_out)[2][2],
-                       auto ndc, const uint32_t* doff, uint32_t dlds, const uint8_t* dbase) {
+                       auto ndc, const uint32_t* doff, uint32_t dlds, const uint8_t* dbase,
+                       auto ndc2, const uint32_t* doff2, uint32_t dlds2, const uint8_t* dbase2) {
     constexpr bool HS = decltype(has_s)::value, HP = decltype(has_p)::value;
-    constexpr int ND = decltype(ndc)::value;
+    constexpr int ND1 = decltype(ndc)::value, ND = ND1 + decltype(ndc2)::value;
     constexpr int NS = HS ? NS_FULL : 0;
     constexpr int NR = NS + NP;
     constexpr int NKOP = HS ? QREGS : 0;  // K operands (each feeds both query blocks)
@@ -542,7 +544,10 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, ND>([&](auto dc) {
         constexpr int dj = decltype(dc)::value;
-        if constexpr (((2 * dj + 1) * NR) / (2 * ND) == r) Loader::dma16(dlds + 1024 * dj, doff[dj], dbase);
+        if constexpr (((2 * dj + 1) * NR) / (2 * ND) == r) {
+          if constexpr (dj < ND1) Loader::dma16(dlds + 1024 * dj, doff[dj], dbase);
+          else Loader::dma16(dlds2 + 1024 * (dj - ND1), doff2[dj - ND1], dbase2);
+        }
       });
       if constexpr (r + LA < NR) load_for(std::integral_constant<int, r + LA>());
       if constexpr (r + 1 < NR) conv_for(std::integral_constant<int, r + 1>());
@@ -564,8 +569,10 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
   };
 
   // ---- the key loop ------------------------------------------------------------------------
-  // Ring: slot s (s >= -1) holds K of tile s+1 and V of tile s, in buffer (s+1) % 3.  Iteration j
-  // reads slot j (scores of tile j+1, P.V of tile j) and fills slot j+2.
+  // Ring: slot s (s >= -1) holds K of tile s+1 and V of tile s, in buffer (s+1) % 4.  Iteration j
+  // reads slot j (scores of tile j+1, P.V of tile j).  Iterations come in pairs: the first of a
+  // pair (j even) fills slots j+2 and j+3 into the two buffers the previous pair read; the second
+  // waits for those loads and ends with the workgroup barrier, one per two key tiles.
   auto tix = [&](int j) { return 2 * (kt0 + j); };  // descriptor of the segment's j-th tile
   // Tile descriptors (first pool row, valid keys) are read with scalar loads one step before
   // they are needed, so no step waits on a scalar load.
@@ -616,14 +623,6 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     if (s + 1 < n) ld.fill_k(kpool, dk.row0, dk.nv, head, H, ka);
     if (s >= 0 && s < n) ld.fill_v(vpool, dv.row0, dv.nv, head, H, va);
   };
-  // wait until only the loads of slot s (issued last) may still be in flight
-  auto wait_all_but_slot = [&](int s) {
-    const bool kpart = s + 1 < n, vpart = s >= 0 && s < n;
-    if (kpart && vpart) wait_vmcnt<KI + VI>();
-    else if (vpart) wait_vmcnt<VI>();
-    else if (kpart) wait_vmcnt<KI>();
-    else wait_vmcnt<0>();
-  };
   auto set_cm = [&](float ksc, float (&cm)[2]) {
     cm[0] = cq[0] * ksc;  // > 0, so scaling commutes with the max
     cm[1] = cq[1] * ksc;
@@ -644,7 +643,7 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
     clear_o();
     // prologue: slots -1, 0, 1 in flight; wait for slot -1 (K of tile 0)
     const Desc d0 = load_desc(0);
-    Desc d1 = load_desc(1), d2 = load_desc(2), d3 = load_desc(3);  // tiles j+1, j+2, j+3 of step j
+    Desc d1 = load_desc(1), d2 = load_desc(2), d3 = load_desc(3), d4 = load_desc(4);  // tiles j+1 .. j+4 of step j
     fill_slot(std::integral_constant<int, 0>(), -1, d0, d0);
     fill_slot(std::integral_constant<int, 1>(), 0, d1, d0);
     if (n > 1) fill_slot(std::integral_constant<int, 2>(), 1, d2, d1);
@@ -673,32 +672,55 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       if constexpr (V8) set_mo(vsc_cur, mo_cur);
       make_p_plain(s0, cm_cur, V8 ? mo_cur : m, V8 ? 1.f / vsc_cur : 1.f, p_a);
     }
-    wait_all_but_slot(1);
+    wait_vmcnt<0>();  // slots 0 and 1: the first pair of iterations has no barrier between them
     __syncthreads();
 
-    // iteration j reads slot j (buffer B, a compile-time constant so that every LDS address is a
-    // per-lane base plus an immediate offset) and refills buffer (B + 2) % 3 with slot j+2
-    auto step = [&](auto bufc, int j) {
+    // iteration j reads slot j (buffer B = (j+1) % 4, a compile-time constant so that every LDS
+    // address is a per-lane base plus an immediate offset).  FILL (j even): slot j+2 (K of tile
+    // j+3, V of tile j+2) goes into buffer (B+2) % 4 during the first half step and slot j+3 (K of
+    // tile j+4, V of tile j+3) into buffer (B+3) % 4 during the second.  Otherwise (j odd) the
+    // iteration ends by waiting for those loads and with the barrier.  Past the segment's end the
+    // descriptors repeat its last tile, so every pair issues the same number of (in-bounds) loads.
+    auto step = [&](auto bufc, auto fillc, int j) {
       constexpr int B = decltype(bufc)::value;
-      // d3 was loaded during the previous step; using it only from here on keeps the compiler
-      // from deriving values from it (and waiting for the load) right after the load
-      d3.row0 = __builtin_amdgcn_readfirstlane(d3.row0);
-      d3.nv = __builtin_amdgcn_readfirstlane(d3.nv);
-      asm volatile("" : "+s"(d3.row0), "+s"(d3.nv));
-      // slot j+2 (K of tile j+3, V of tile j+2) is filled from inside the two half steps; past
-      // the segment's end the descriptors repeat its last tile, so every step issues the same
-      // number of (in-bounds) loads and the wait below is a constant
-      constexpr int FB = (B + 2) % NBUF;
-      // rare: a chunk's last tile (an e4m3 V block is always whole: its tail codes are 0)
-      const bool k_ragged = d3.nv < BN, v_ragged = !V8 && d2.nv < BN;
-      if (k_ragged) ld.set_k(d3.nv, head, H);
-      if (v_ragged) ld.set_v(d2.nv, head, H);
-      const uint8_t* fkb = kpool + (size_t)d3.row0 * H * Loader::KB;
-      const uint8_t* fvb = Loader::v_base(vpool, d2.row0, head, H);
-      const uint32_t fkl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[FB] + ld.wave_u * KI * 1024;
-      const uint32_t fvl = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[FB] + ld.wave_u * VI * 1024;
+      constexpr bool FILL = decltype(fillc)::value;
+      // d4 was loaded during the previous step; using it only from here on keeps the compiler
+      // from deriving values from it (and waiting for the load) right after the load.  The fill
+      // descriptors are pinned to scalar registers here: the loop's four exits otherwise let the
+      // compiler carry them around the loop in vector registers.
+      auto pin = [](Desc& d) {
+        d.row0 = __builtin_amdgcn_readfirstlane(d.row0);
+        d.nv = __builtin_amdgcn_readfirstlane(d.nv);
+        asm volatile("" : "+s"(d.row0), "+s"(d.nv));
+      };
+      pin(d2);
+      pin(d3);
+      pin(d4);
+      constexpr int FB2 = (B + 2) % NBUF, FB3 = (B + 3) % NBUF;
+      constexpr int NK = FILL ? KI : 0, NV = FILL ? VI : 0;
+      const uint8_t* fkb2 = kpool + (size_t)d3.row0 * H * Loader::KB;
+      const uint8_t* fvb2 = Loader::v_base(vpool, d2.row0, head, H);
+      const uint8_t* fkb3 = kpool + (size_t)d4.row0 * H * Loader::KB;
+      const uint8_t* fvb3 = Loader::v_base(vpool, d3.row0, head, H);
+      const uint32_t fkl2 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[FB2] + ld.wave_u * KI * 1024;
+      const uint32_t fvl2 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[FB2] + ld.wave_u * VI * 1024;
+      const uint32_t fkl3 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_k[FB3] + ld.wave_u * KI * 1024;
+      const uint32_t fvl3 = (uint32_t)(uintptr_t)(WF_LDS void*)smem_v[FB3] + ld.wave_u * VI * 1024;
+      // rare: a chunk's last tile among those filled (an e4m3 V block is always whole: its tail
+      // codes are 0); the fill offsets are patched for it and restored afterwards
+      const int nk2 = d3.nv, nv2 = d2.nv, nk3 = d4.nv, nv3 = d3.nv;  // valid keys of the filled tiles
+      bool k_ragged = false, v_ragged = false;
+      auto patch = [&](int nk, int nv) {
+        if (k_ragged) ld.set_k(BN, head, H);
+        if (v_ragged) ld.set_v(BN, head, H);
+        k_ragged = nk < BN;
+        v_ragged = !V8 && nv < BN;
+        if (k_ragged) ld.set_k(nk, head, H);
+        if (v_ragged) ld.set_v(nv, head, H);
+      };
+      if constexpr (FILL) patch(nk2, nv2);
       // descriptors for the next step
-      const Desc d4 = load_desc(j + 4);
+      const Desc d5 = load_desc(j + 5);
       const float ksc_n2 = k_scale_of(j + 2, d2);
       const float vsc_n2 = v_scale_of(d2);
       const int nv_nxt = d1.nv;
@@ -716,22 +738,30 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         f32x16 s_n0[2];
         bf16x8 p_1[2][2];
         half_step(std::true_type(), std::true_type(), sk, 0, s_n0, sv, 0, p_a, s_a, cm_cur, V8 ? mo_cur : m, p_1,
-                  std::integral_constant<int, KI>(), ld.koff, fkl, fkb);
+                  std::integral_constant<int, NK>(), ld.koff, fkl2, fkb2, std::integral_constant<int, NV>(), ld.voff,
+                  fvl2, fvb2);
         if (nv_nxt < BN) {
           score_drain(s_n0);
           mask_half(s_n0, 0, nv_nxt);
         }
+        if constexpr (FILL) patch(nk3, nv3);
         // B: scores of tile j+1 half 1; P.V of tile j half 1; P of tile j+1 half 0
         half_step(std::true_type(), std::true_type(), sk, 1, s_a, sv, 1, p_1, s_n0, cm_nxt, V8 ? mo_nxt : m, p_a,
-                  std::integral_constant<int, VI>(), ld.voff, fvl, fvb);
+                  std::integral_constant<int, NK>(), ld.koff, fkl3, fkb3, std::integral_constant<int, NV>(), ld.voff,
+                  fvl3, fvb3);
         __builtin_amdgcn_sched_barrier(0);
         row_sums(p_1, V8 ? 1.f / vsc_cur : 1.f);
         row_sums(p_a, V8 ? 1.f / vsc_nxt : 1.f);
-      } else {  // a wave without query rows still does its share of the fills
+      } else if constexpr (FILL) {  // a wave without query rows still does its share of the fills
 #pragma unroll
-        for (int i = 0; i < KI; ++i) Loader::dma16(fkl + 1024 * i, ld.koff[i], fkb);
+        for (int i = 0; i < KI; ++i) Loader::dma16(fkl2 + 1024 * i, ld.koff[i], fkb2);
 #pragma unroll
-        for (int i = 0; i < VI; ++i) Loader::dma16(fvl + 1024 * i, ld.voff[i], fvb);
+        for (int i = 0; i < VI; ++i) Loader::dma16(fvl2 + 1024 * i, ld.voff[i], fvb2);
+        patch(nk3, nv3);
+#pragma unroll
+        for (int i = 0; i < KI; ++i) Loader::dma16(fkl3 + 1024 * i, ld.koff[i], fkb3);
+#pragma unroll
+        for (int i = 0; i < VI; ++i) Loader::dma16(fvl3 + 1024 * i, ld.voff[i], fvb3);
       }
       if (k_ragged) ld.set_k(BN, head, H);
       if (v_ragged) ld.set_v(BN, head, H);
@@ -747,11 +777,14 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
       d1 = d2;
       d2 = d3;
       d3 = d4;
+      d4 = d5;
       ksc_nxt = ksc_n2;
-      wait_vmcnt<KI + VI>();  // slot j+1 has landed (only slot j+2's loads may be in flight)
-      __syncthreads();
+      if constexpr (!FILL) {
+        wait_vmcnt<0>();  // slots j+1 and j+2, filled by the previous iteration, have landed
+        __syncthreads();
+      }
     };
-    // last tile (slot n-1, buffer n % 3): P.V only.  One instantiation with a runtime buffer, so
+    // last tile (slot n-1, buffer n % 4): P.V only.  One instantiation with a runtime buffer, so
     // that O flows through a single path (a branch per buffer would make the register allocator
     // copy O between AGPRs, and such copies cannot be ordered after the asm MFMAs that write O).
     auto last = [&](int b) {
@@ -764,19 +797,25 @@ __device__ __forceinline__ void run_segment(const FwdParams& p, const int32_t* i
         f32x16 dummy[2];
         bf16x8 p_1[2][2], p_unused[2][2];
         half_step(std::false_type(), std::true_type(), nullptr, 0, dummy, sv, 0, p_a, s_a, cm_cur, V8 ? mo_cur : m,
-                  p_1, std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
+                  p_1, std::integral_constant<int, 0>(), nullptr, 0u, nullptr, std::integral_constant<int, 0>(), nullptr,
+                  0u, nullptr);
         half_step(std::false_type(), std::false_type(), nullptr, 0, dummy, sv, 1, p_1, s_a, cm_cur, V8 ? mo_cur : m,
-                  p_unused, std::integral_constant<int, 0>(), nullptr, 0u, nullptr);
+                  p_unused, std::integral_constant<int, 0>(), nullptr, 0u, nullptr, std::integral_constant<int, 0>(),
+                  nullptr, 0u, nullptr);
         row_sums(p_1, V8 ? 1.f / vsc_cur : 1.f);
       }
     };
+    // (a loop that ends after the first of a pair needs no barrier: the last tile's slot was
+    // filled before the previous pair's barrier, and the pending loads go to other buffers)
     for (int j = 0;;) {
       if (j + 1 >= n) break;
-      step(std::integral_constant<int, 1>(), j++);
+      step(std::integral_constant<int, 1>(), std::true_type(), j++);
       if (j + 1 >= n) break;
-      step(std::integral_constant<int, 2>(), j++);
+      step(std::integral_constant<int, 2>(), std::false_type(), j++);
       if (j + 1 >= n) break;
-      step(std::integral_constant<int, 0>(), j++);
+      step(std::integral_constant<int, 3>(), std::true_type(), j++);
+      if (j + 1 >= n) break;
+      step(std::integral_constant<int, 0>(), std::false_type(), j++);
     }
     last(n % NBUF);
     wait_vmcnt<0>();  // the fills issued past the segment's end land before the ring is reused
