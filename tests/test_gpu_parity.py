@@ -155,6 +155,32 @@ def test_degenerate_tables(B, O):
             check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
+def test_long_prefix_many_pieces(B, O):
+    """A long rollout at the sizes the kernel's bookkeeping is stressed by: 64 chunks of 1,024
+    tokens on 256-token pages (65,536 visible keys, 1,024 key tiles per item), one head, the last
+    chunk's 1,024 queries: four items over all the workgroups, so the default plan cuts each item
+    into dozens of pieces (merged in many batches of four), and a whole-item plan runs segments
+    of 1,024 tiles.  Every element against the oracle, both plans, bf16 and e4m3."""
+    rng = np.random.default_rng(41)
+    nch = 64
+    t = make_table([1024] * nch, list(range(nch)), [nch - 1], 256, 1, 128, shuffle_rng=rng, spare=3)
+    c = fill_case("long_prefix", t, rng, torch.bfloat16)
+    ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, want_sumw2=True)
+    for split in (0, 1):
+        print(f"[case] 64-chunk prefix split_k={split}", flush=True)
+        out, lse, att = run(B, c, split_k=split)
+        if split == 0:
+            assert int(att.plan.describe(0)[6]) >= 32  # most pieces of one item
+        check_bf16(f64(out), ref, f"64-chunk prefix split {split}")
+        check_lse(f64(lse).T, ref_lse, ref_w2)
+    print("[case] 64-chunk prefix e4m3", flush=True)
+    out8, lse8 = run_fp8(B, c)
+    qdq, kdq = _dequantized_case(O, c)
+    ref8, ref8_lse, ref8_w2 = O.attn_rows(t, qdq, kdq, c.v_pool, want_sumw2=True)
+    check_bf16(f64(out8), ref8, "64-chunk prefix e4m3 (dequantized oracle)")
+    check_lse(f64(lse8).T, ref8_lse, ref8_w2)
+
+
 def _random_table(rng):
     """A chunk table drawn at random: 1-6 chunks of 1-64, 65-300 or 301-500 tokens; a permutation
     of orders, or (half the time) orders with ties; a random subset of query chunks in random
