@@ -333,7 +333,7 @@ extern "C" wfattn_status wfattn_qkv_rope_publish(const wfattn_plan_t* plan, int3
       INT32_MAX)
     return WFATTN_ERR_RANGE;
   if (!ws) return WFATTN_ERR_WORKSPACE;
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(cos_t, 4) || !aligned(sin_t, 4) || !aligned(q_out, 16) ||
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(cos_t, 16) || !aligned(sin_t, 16) || !aligned(q_out, 16) ||
       !aligned(q8, 16) || !aligned(q_scale, 4) || !aligned(k_pool, 16) || !aligned(k8_pool, 16) ||
       !aligned(k_scale, 4) || !aligned(v_pool, 16) || !aligned(flags, 4) || !aligned(ws, 256))
     return WFATTN_ERR_UNSUPPORTED;

@@ -17,13 +17,11 @@
 // is a plain 16-byte LDS read of a token row, the W operand a pair of transposed reads
 // (ds_read_b64_tr_b16) of the row-major W slice, as the attention kernel reads V^T.
 //
-// Epilogue.  Accumulator register j of lane l holds token 8(j/4) + 4(l/32) + j%4 of a 32-token
-// block and channel l%32 of a 32-channel block, so the two channels of a rotary pair (2i, 2i+1)
-// sit in neighbouring lanes: one DPP swap brings the partner in.  The rotated (or, for v, plain)
-// values are rounded to bf16 and staged in LDS as the [256 tokens][d] tile; then wave w takes the
-// 64-token tile w (one page-aligned 64-row block of the pool, one 64-row Q-scale block), one token
-// row per lane, and writes bf16 rows or quantizes the tile as one e4m3 block (the rule of
-// wfattn_quantize_fp8, over the bf16 values).
+// Epilogue.  The fp32 accumulators are staged in LDS as the [256 tokens][d] tile; then wave w takes
+// the 64-token tile w (one page-aligned 64-row block of the pool, one 64-row Q-scale block), one
+// token row per lane: the lane reads its row and the token's angle row (cos, sin: contiguous, 16
+// bytes at a time), rotates q and k pair by pair, rounds to bf16, and writes the bf16 row or
+// quantizes the tile as one e4m3 block (the rule of wfattn_quantize_fp8, over the bf16 values).
 #include "blockq.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
@@ -71,8 +69,11 @@ __device__ __forceinline__ float rotate_one(float own, float other, float c, flo
   return a - b;
 }
 
-// x slice in LDS: row r (a token) is 128 bytes, granule g stored at g ^ (r mod 8)
-__device__ __forceinline__ int xoff(int r, int g) { return r * 128 + ((g ^ (r & 7)) << 4); }
+// x slice in LDS: row r (a token) is 128 bytes, two rows per 256-byte line of the 64 banks;
+// granule g is stored at g ^ ((r / 2) mod 8), so the 16 lanes of one ds_read_b128 phase (rows
+// r .. r+15, one granule) touch 16 distinct 16-byte bank groups
+__device__ __forceinline__ int xswz(int r, int g) { return g ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int xoff(int r, int g) { return r * 128 + (xswz(r, g) << 4); }
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
@@ -81,8 +82,20 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
   if (hdr[H_NONCE_LO] != (int32_t)p.nonce_lo || hdr[H_NONCE_HI] != (int32_t)p.nonce_hi) return;
   __shared__ __attribute__((aligned(16))) uint8_t smem[NST * (G::XBYTES + G::WBYTES)];
   const int H = p.heads, C = p.hidden, n = p.tokens;
-  const int t0 = blockIdx.x * QBM;
-  const int role = blockIdx.y / H, head = blockIdx.y % H;
+  // Workgroup -> (token tile tt, role-and-head column block rh).  The hardware hands consecutive
+  // workgroups to the 8 XCDs in turn; workgroup w takes the next pair of XCD w % 8's contiguous
+  // share of all pairs, and the pairs are ordered in blocks of 8 column blocks by token tile, so
+  // the ~32 workgroups an XCD runs at once cover about 4 token tiles x 8 column blocks and share
+  // their x and W slices in its L2.  (Any bijection is correct; this one only places the work.)
+  constexpr int NX = 8, RB = 8;
+  const int ntt = (n + QBM - 1) / QBM, nrh = 3 * H, nrb = (nrh + RB - 1) / RB;
+  const int nwg = (int)gridDim.x, xcd = (int)blockIdx.x % NX, kx = (int)blockIdx.x / NX;
+  const int pair = xcd * (nwg / NX) + (xcd < nwg % NX ? xcd : nwg % NX) + kx;
+  const int rb = min(pair / (ntt * RB), nrb - 1);
+  const int rem = pair - rb * ntt * RB, width = rb < nrb - 1 ? RB : nrh - rb * RB;
+  const int tt = rem / width, rh = rb * RB + rem % width;
+  const int t0 = tt * QBM;
+  const int role = rh / H, head = rh % H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wr = wave / G::WC, wc = wave % G::WC;
   const size_t ldw = (size_t)3 * H * D;
@@ -99,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
   for (int i = 0; i < G::XG; ++i) {
     const int ch = (wave * G::XG + i) * 64 + lane, r = ch >> 3, pg = ch & 7;
     const int tok = t0 + r < n ? t0 + r : n - 1;  // rows past the chunk re-read its last token
-    xo_off[i] = (uint32_t)((size_t)tok * C * 2 + 16 * (pg ^ (r & 7)));
+    xo_off[i] = (uint32_t)((size_t)tok * C * 2 + 16 * xswz(r, pg));
   }
 #pragma unroll
   for (int i = 0; i < G::WG; ++i) {
@@ -168,8 +181,12 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
   wait_vmcnt<0>();  // the reloads issued past the end land before the LDS is reused
   __syncthreads();
 
-  // ---- epilogue: rotate (q, k), round to bf16, stage the [256][D] tile in LDS ------------------
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // the GEMM's buffers are free now
+  // ---- epilogue: stage the fp32 tile [256 tokens][D] in LDS (the GEMM's buffers are free now) -----
+  // Row stride D+8 floats: the two halves of a wave store rows four apart, which the padding puts
+  // 32 banks apart.
+  constexpr int FS = D + 8;
+  static_assert(QBM * FS * 4 <= NST * (G::XBYTES + G::WBYTES), "the fp32 tile fits in the GEMM's LDS");
+  float* ftile = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int tb = 0; tb < G::TB; ++tb)
 #pragma unroll
@@ -178,57 +195,82 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = G::TOKW * wr + 32 * tb + 8 * (j / 4) + 4 * hi + (j % 4);
-        float y = acc[tb][cb][j];
-        // the partner of channel ch in its rotary pair is ch ^ 1: the neighbouring lane
-        const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, false));
-        if (role < 2) {
-          const int tok = t0 + r < n ? t0 + r : n - 1;
-          const float c = p.cos_t[(size_t)tok * (D / 2) + (ch >> 1)];
-          const float s = p.sin_t[(size_t)tok * (D / 2) + (ch >> 1)];
-          y = rotate_one(y, other, c, s, ch & 1);
-        }
-        tile[r * D + ch] = (uint16_t)(pack2_bf16(y, 0.f) & 0xffffu);
+        ftile[r * FS + ch] = acc[tb][cb][j];
       }
     }
   __syncthreads();
 
-  // ---- epilogue: wave w writes the 64-token tile w, one token row per lane ----------------------
-  const int t = blockIdx.x * (QBM / 64) + wave;  // tile of the chunk
+  // ---- epilogue: wave w takes the 64-token tile w (one page-aligned 64-row block of the pool, one
+  // 64-row Q-scale block).  D/8 lanes share a token row, one 16-byte granule (8 channels, 4 rotary
+  // pairs) each, so every read of the angles and every row write is a contiguous run per row;
+  // a pass covers 64 / (D/8) rows.
+  constexpr int GPR = D / 8, RPI = 64 / GPR, NIT = 64 / RPI;
+  const int t = tt * (QBM / 64) + wave;  // tile of the chunk
   if (t * 64 >= n) return;
   const int32_t first_tile = p.blob[hdr[H_OFF_CHUNKS] + p.chunk * kChunkInts];
   const int32_t* td = p.blob + hdr[H_OFF_TILES] + (first_tile + t) * kTileInts;
   const int64_t row0 = td[0];
   const int nv = td[1];
-  const int r = 64 * wave + lane;  // row of the staged tile
-  const bool ok = lane < nv;
-  const uint4* src = reinterpret_cast<const uint4*>(tile + r * D);
-  const int64_t tok = (int64_t)t * 64 + lane;
-  // bf16 rows
-  uint16_t* dst = nullptr;
-  if (role == 0) dst = p.q_out ? p.q_out + (tok * H + head) * D : nullptr;
-  else if (role == 1) dst = p.k_pool ? p.k_pool + ((row0 + lane) * H + head) * D : nullptr;
-  else dst = p.v_pool + ((row0 + lane) * H + head) * D;
-  if (dst && ok) {
+  const int gi = lane % GPR, ri = lane / GPR;
+  // q and k: each channel pair (2i, 2i+1) rotated by the token's angle i, every product and sum
+  // rounded to fp32 on its own; then every value rounded to bf16
+  uint4 val[NIT];
+  auto tile_row = [&](int it) { return ftile + (64 * wave + RPI * it + ri) * FS + 8 * gi; };
+  if (role < 2) {  // uniform: every angle load is issued before the first is used
+    float4 cv[NIT], sn[NIT];
 #pragma unroll
-    for (int g = 0; g < D / 8; ++g) reinterpret_cast<uint4*>(dst)[g] = src[g];
+    for (int it = 0; it < NIT; ++it) {
+      const int row = RPI * it + ri;
+      const int64_t tc = (int64_t)t * 64 + (row < nv ? row : 0);  // rows past the chunk: a valid angle row
+      cv[it] = *reinterpret_cast<const float4*>(p.cos_t + tc * (D / 2) + 4 * gi);
+      sn[it] = *reinterpret_cast<const float4*>(p.sin_t + tc * (D / 2) + 4 * gi);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const float4 a = *reinterpret_cast<const float4*>(tile_row(it));
+      const float4 b = *reinterpret_cast<const float4*>(tile_row(it) + 4);
+      float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const float c[4] = {cv[it].x, cv[it].y, cv[it].z, cv[it].w};
+      const float sv[4] = {sn[it].x, sn[it].y, sn[it].z, sn[it].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = y[2 * i], x1 = y[2 * i + 1];
+        y[2 * i] = rotate_one(x0, x1, c[i], sv[i], 0);
+        y[2 * i + 1] = rotate_one(x1, x0, c[i], sv[i], 1);
+      }
+      val[it] = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]), pack2_bf16(y[4], y[5]),
+                           pack2_bf16(y[6], y[7]));
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const float4 a = *reinterpret_cast<const float4*>(tile_row(it));
+      const float4 b = *reinterpret_cast<const float4*>(tile_row(it) + 4);
+      val[it] = make_uint4(pack2_bf16(a.x, a.y), pack2_bf16(a.z, a.w), pack2_bf16(b.x, b.y), pack2_bf16(b.z, b.w));
+    }
+  }
+  // destination row of tile row `row`: bf16 q, K (bf16 pool) or V
+  auto bf16_row = [&](int row) -> uint16_t* {
+    const int64_t tok = (int64_t)t * 64 + row;
+    if (role == 0) return p.q_out ? p.q_out + (tok * H + head) * D : nullptr;
+    if (role == 1) return p.k_pool ? p.k_pool + ((row0 + row) * H + head) * D : nullptr;
+    return p.v_pool + ((row0 + row) * H + head) * D;
+  };
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int row = RPI * it + ri;
+    uint16_t* dst = bf16_row(row);
+    if (dst && row < nv) reinterpret_cast<uint4*>(dst)[gi] = val[it];
   }
   // e4m3 rows: q8 (role 0) or the e4m3 K pool (role 1), the tile quantized as one block
-  uint8_t* dst8 = nullptr;
-  float* sc = nullptr;
-  if (role == 0 && p.q8) {
-    dst8 = p.q8 + (tok * H + head) * D;
-    sc = p.q_scale + (size_t)t * H + head;
-  } else if (role == 1 && p.k8_pool) {
-    dst8 = p.k8_pool + ((row0 + lane) * H + head) * D;
-    sc = p.k_scale + (row0 / 64) * H + head;
-  }
-  if (dst8) {  // uniform across the wave
+  const bool q8 = role == 0 && p.q8, k8 = role == 1 && p.k8_pool;
+  if (q8 || k8) {  // uniform across the wave
     float amax = 0.f;
-    if (ok) {
 #pragma unroll
-      for (int g = 0; g < D / 8; ++g) {
+    for (int it = 0; it < NIT; ++it) {
+      if (RPI * it + ri < nv) {
         float v[8];
-        unpack8(src[g], v);
+        unpack8(val[it], v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float a = fabsf(v[e]);
@@ -246,12 +288,16 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
       scale = __fdiv_rn(amax, 448.f);
       mult = __fdiv_rn(448.f, amax);
     }
-    if (lane == 0) *sc = scale;
-    if (ok) {
+    if (lane == 0) {
+      if (q8) p.q_scale[(size_t)t * H + head] = scale;
+      else p.k_scale[(row0 / 64) * H + head] = scale;
+    }
 #pragma unroll
-      for (int g = 0; g < D / 8; ++g) {
+    for (int it = 0; it < NIT; ++it) {
+      const int row = RPI * it + ri;
+      if (row < nv) {
         float v[8];
-        unpack8(src[g], v);
+        unpack8(val[it], v);
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -264,7 +310,9 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-        reinterpret_cast<uint2*>(dst8)[g] = make_uint2((uint32_t)w0, (uint32_t)w1);
+        const int64_t tok = (int64_t)t * 64 + row;
+        uint8_t* dst8 = q8 ? p.q8 + (tok * H + head) * D : p.k8_pool + ((row0 + row) * H + head) * D;
+        reinterpret_cast<uint2*>(dst8)[gi] = make_uint2((uint32_t)w0, (uint32_t)w1);
       }
     }
   }
@@ -273,10 +321,10 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_publish_kernel(QkvParams p) {
 }  // namespace
 
 hipError_t launch_qkv_rope_publish(const QkvParams& p, int32_t head_dim, hipStream_t s) {
-  const unsigned gx = (unsigned)((p.tokens + QBM - 1) / QBM), gy = (unsigned)(3 * p.heads);
+  const unsigned nwg = (unsigned)((p.tokens + QBM - 1) / QBM) * (unsigned)(3 * p.heads);
   if (p.tokens > 0) {
-    if (head_dim == 128) hipLaunchKernelGGL(qkv_rope_publish_kernel<128>, dim3(gx, gy), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(qkv_rope_publish_kernel<64>, dim3(gx, gy), dim3(256), 0, s, p);
+    if (head_dim == 128) hipLaunchKernelGGL(qkv_rope_publish_kernel<128>, dim3(nwg), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(qkv_rope_publish_kernel<64>, dim3(nwg), dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
