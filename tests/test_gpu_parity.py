@@ -411,6 +411,40 @@ def test_publish_then_gated_forward_on_two_streams(B, O):
     check_lse(f64(lse).T, ref_lse, ref_w2)
 
 
+def test_gate_waits_for_a_flag_raised_while_it_polls(B, O):
+    """The flags live in pinned host memory, and the query chunk's flag is down when the gated
+    forward starts.  The host raises it 50 ms later, while the kernel polls.  So every item's
+    first poll fails and the gate takes its wait path on the device: poll, sleep, poll again,
+    then the acquire fence.  The call lasts at least the delay, reports nothing, and matches the
+    oracle."""
+    import time
+    c = medium_case("wan13b_task", seed=29)
+    t = c.table
+    q, k, v = to_dev(c)
+    att = B.Attention(t)
+    flags = torch.tensor([5, 5, 5, 0], dtype=torch.int32).pin_memory()  # read by the kernel over the fabric
+    need = torch.full((4,), 5, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((t.lq, t.num_heads, t.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((t.num_heads, t.lq), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print("[case] gated forward with chunk 3's flag down; the host raises it 50 ms later", flush=True)
+    e0.record()
+    # at most 200000 polls about 2 us apart: the wait ends even if the flag never rose
+    B.wfattn_fwd_gated(att.plan, q, k, v, out, lse, att.ws, flags, need, 200000, status)
+    e1.record()
+    time.sleep(0.05)
+    flags[3] = 5
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    waited_ms = e0.elapsed_time(e1)
+    assert waited_ms >= 40.0, waited_ms  # the kernel was polling before the flag rose
+    ref, ref_lse, ref_w2 = O.attn_rows(t, c.q, c.k_pool, c.v_pool, want_sumw2=True)
+    check_bf16(f64(out), ref, "gate-waited")
+    check_lse(f64(lse).T, ref_lse, ref_w2)
+
+
 def test_gate_skips_items_of_unpublished_chunks(B, O):
     """Query chunks with different prefixes; the noisiest chunk's flag is short.  Its items are
     skipped after a bounded poll (their rows keep the caller's sentinel), bit 0 of the status is
