@@ -82,18 +82,23 @@ __global__ __launch_bounds__(256) void rope_publish_kernel(RopeParams p) {
     if (r >= nv) continue;
     const int64_t tok = (int64_t)t * 64 + r;
     const uint16_t* src = p.qkv + (tok * 3 * H + head) * D + 8 * g;
-    float x[8];
-    uint4 w;
+    // the row's q, k, v and angles are all loaded before its first store (the compiler would
+    // otherwise keep the k and v loads behind the q store, which may alias them as far as it knows)
+    const uint4 xq = *reinterpret_cast<const uint4*>(src);
+    const uint4 xk = *reinterpret_cast<const uint4*>(src + (size_t)H * D);
+    const uint4 xv = *reinterpret_cast<const uint4*>(src + (size_t)2 * H * D);
     const float4 c = *reinterpret_cast<const float4*>(p.cos_t + tok * (D / 2) + 4 * g);
     const float4 s = *reinterpret_cast<const float4*>(p.sin_t + tok * (D / 2) + 4 * g);
-    unpack8(*reinterpret_cast<const uint4*>(src), x);
+    float x[8];
+    uint4 w;
+    unpack8(xq, x);
     rotate8(x, c, s, qv[it], w);
     if (p.q_out) *reinterpret_cast<uint4*>(p.q_out + (tok * H + head) * D + 8 * g) = w;
-    unpack8(*reinterpret_cast<const uint4*>(src + (size_t)H * D), x);
+    unpack8(xk, x);
     rotate8(x, c, s, kv[it], w);
     const size_t prow = ((size_t)(row0 + r) * H + head) * D + 8 * g;
     if (p.k_pool) *reinterpret_cast<uint4*>(p.k_pool + prow) = w;
-    *reinterpret_cast<uint4*>(p.v_pool + prow) = *reinterpret_cast<const uint4*>(src + (size_t)2 * H * D);
+    *reinterpret_cast<uint4*>(p.v_pool + prow) = xv;
   }
   if (p.q8)
     quantize_regs<D>(qv, nv, (size_t)H * D, p.q8 + ((size_t)t * 64 * H + head) * D, p.q_scale + (size_t)t * H + head);
